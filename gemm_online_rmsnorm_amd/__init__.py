@@ -1,0 +1,144 @@
+"""MI355X (gfx950) low-rank decoder-block hot path.
+
+Python binding of liblrblock.so. The functions here only marshal torch
+tensors into the C ABI of include/lr_block.h (device pointers, sizes and the
+current HIP stream); every step of the block runs in the library's kernels.
+Torch supplies device memory and streams. If the library has not been built
+the first call raises; there is no other implementation to fall back on.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    LR_BF16, LR_EPI_ADD_RESIDUAL, LR_EPI_NONE, LR_EPI_ROW_SCALE, LR_EPI_SWIGLU_PAIR, LR_F32,
+    LR_LAYOUT_NN, LR_LAYOUT_NT, LR_LAYOUT_TN, LR_STAGE_ALL, LR_STAGE_POST_ATTN,
+    LR_STAGE_PRE_ATTN, LRError, lr_block_shape,
+)
+
+WEIGHT_FIELDS = ("gamma1", "gamma2", "A_qkv", "B_q", "B_k", "B_v", "A_o", "B_o",
+                 "A_gu", "B_g", "B_u", "A_dn", "B_dn")
+SAVED_FIELDS = ("qkv_r", "o_r", "gu_r", "d_r", "rms1", "rms2")
+PARTIAL_FIELDS = ("P_qkv", "P_gu", "ss1", "ss2")
+
+_TORCH = {LR_F32: torch.float32, LR_BF16: torch.bfloat16}
+
+
+def torch_dtype(dtype: int) -> torch.dtype:
+    return _TORCH[dtype]
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor is not on a GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor is not contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, device=None) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def block_shape(T, d, r, d_ff, d_norm=None, n_panels=1, n_heads=1, eps=1e-5, dtype=LR_BF16,
+                emit_partials=False) -> lr_block_shape:
+    return lr_block_shape(T=T, d=d, r=r, d_ff=d_ff, d_norm=d_norm or d, n_panels=n_panels,
+                          n_heads=n_heads, eps=eps, dtype=dtype,
+                          emit_partials=int(bool(emit_partials)))
+
+
+def workspace_bytes(shape: lr_block_shape, is_bwd: bool) -> int:
+    return int(_lib.load().lr_block_workspace_bytes(ctypes.byref(shape), int(bool(is_bwd))))
+
+
+def alloc_workspace(shape: lr_block_shape, is_bwd: bool, device="cuda") -> torch.Tensor:
+    n = workspace_bytes(shape, is_bwd)
+    if n == 0:
+        raise ValueError("invalid block shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _struct(cls, fields, d):
+    s = cls()
+    if d is not None:
+        for f in fields:
+            setattr(s, f, _ptr(d.get(f)))
+    return s
+
+
+def block_fwd(shape, W, X, O, out, saved, partials=None, stage=LR_STAGE_ALL, ws=None,
+              stream=None) -> None:
+    """lr_block_fwd. W, out (Q, K, V, Y), saved, partials: dicts of tensors."""
+    lib = _lib.load()
+    w = _struct(_lib.lr_block_weights, WEIGHT_FIELDS, W)
+    sv = _struct(_lib.lr_block_saved, SAVED_FIELDS, saved)
+    pt = _struct(_lib.lr_block_partials, PARTIAL_FIELDS, partials) if partials else None
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _lib.check(lib.lr_block_fwd(
+        ctypes.byref(shape), ctypes.byref(w), _ptr(X), _ptr(O), _ptr(out.get("Q")),
+        _ptr(out.get("K")), _ptr(out.get("V")), _ptr(out.get("Y")), ctypes.byref(sv),
+        ctypes.byref(pt) if pt is not None else None, stage, _ptr(ws), nbytes,
+        _stream(stream, X.device)))
+
+
+def block_bwd(shape, W, X, O, saved, dY, dQ, dK, dV, dX, dO, grads, stage=LR_STAGE_ALL,
+              ws=None, stream=None) -> None:
+    """lr_block_bwd. grads: dict of fp32 tensors keyed like the weights."""
+    lib = _lib.load()
+    w = _struct(_lib.lr_block_weights, WEIGHT_FIELDS, W)
+    sv = _struct(_lib.lr_block_saved, SAVED_FIELDS, saved)
+    g = _struct(_lib.lr_block_grads, WEIGHT_FIELDS, grads)
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _lib.check(lib.lr_block_bwd(
+        ctypes.byref(shape), ctypes.byref(w), _ptr(X), _ptr(O), ctypes.byref(sv), _ptr(dY),
+        _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dX), _ptr(dO), ctypes.byref(g), stage, _ptr(ws),
+        nbytes, _stream(stream, X.device)))
+
+
+def grouped_lowrank_gemm(pairs, dtype, layout=LR_LAYOUT_NT, epilogue=LR_EPI_NONE,
+                         stream=None) -> None:
+    """lr_grouped_lowrank_gemm. pairs: list of dicts with M, N, K, X, W, Y,
+    optional ldx, ldw, ldy (default: the contiguous row lengths), aux, ldaux."""
+    lib = _lib.load()
+    arr = (_lib.lr_gemm_pair * len(pairs))()
+    dev = None
+    for i, p in enumerate(pairs):
+        M, N, K = p["M"], p["N"], p["K"]
+        ldx = p.get("ldx", M if layout == LR_LAYOUT_TN else K)
+        ldw = p.get("ldw", K if layout == LR_LAYOUT_NT else N)
+        aux = p.get("aux")
+        arr[i] = _lib.lr_gemm_pair(M, N, K, _ptr(p["X"]), ldx, _ptr(p["W"]), ldw, _ptr(p["Y"]),
+                                   p.get("ldy", N), _ptr(aux), p.get("ldaux", N))
+        dev = p["X"].device
+    _lib.check(lib.lr_grouped_lowrank_gemm(len(pairs), arr, dtype, layout, epilogue,
+                                           _stream(stream, dev)))
+
+
+def online_rmsnorm_gemm(X, gamma, A, out, *, n_panels=1, d_norm=None, eps=1e-5, rms_out=None,
+                        ss_out=None, emit_partial=False, ws=None, stream=None) -> None:
+    """lr_online_rmsnorm_gemm with contiguous X [T, d], A [N, d], out [T, N]."""
+    lib = _lib.load()
+    T, d = X.shape
+    N = A.shape[0]
+    dtype = LR_F32 if X.dtype == torch.float32 else LR_BF16
+    if gamma is not None and ws is None:
+        ws = torch.empty(int(lib.lr_online_rmsnorm_gemm_workspace_bytes(N, d, dtype)),
+                         dtype=torch.uint8, device=X.device)
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _lib.check(lib.lr_online_rmsnorm_gemm(
+        T, d, N, n_panels, d_norm or d, eps, _ptr(X), d, _ptr(gamma), _ptr(A), d, _ptr(out), N,
+        _ptr(rms_out), _ptr(ss_out), int(bool(emit_partial)), dtype, _ptr(ws), nbytes,
+        _stream(stream, X.device)))
+
+
+def version() -> str:
+    return _lib.load().lr_version().decode()

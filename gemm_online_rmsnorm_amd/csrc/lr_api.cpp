@@ -1,0 +1,930 @@
+// C ABI of the low-rank block library: argument validation, workspace
+// carving and the launch sequences of the forward and backward passes.
+//
+// Every check runs before anything is enqueued; a failed check returns a
+// negative status with a message for lr_last_error() and no HIP call is
+// made, so argument errors are reported identically on hosts without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/lr_block.h"
+#include "lr_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(LR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define LR_HIP(call, what)                        \
+  do {                                            \
+    hipError_t e_ = (call);                       \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+size_t elem_size(int dtype) { return dtype == LR_F32 ? 4 : 2; }
+int vec_elems(int dtype) { return dtype == LR_F32 ? 4 : 8; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+// Workspace carving: each region starts on a 256-byte boundary.
+struct Carver {
+  unsigned char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<unsigned char*>(b)) {}
+  void* take(size_t bytes) {
+    off = (off + 255) & ~size_t(255);
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+int check_shape(const lr_block_shape* s) {
+  if (!s) return fail(LR_ERR_INVALID_ARG, "shape is NULL");
+  if (s->dtype != LR_F32 && s->dtype != LR_BF16)
+    return fail(LR_ERR_INVALID_ARG, "dtype %d is neither LR_F32 nor LR_BF16", s->dtype);
+  const int64_t dims[5] = {s->T, s->d, s->r, s->d_ff, s->d_norm};
+  const char* names[5] = {"T", "d", "r", "d_ff", "d_norm"};
+  for (int i = 0; i < 5; ++i)
+    if (dims[i] < 1 || dims[i] > kMaxDim)
+      return fail(LR_ERR_INVALID_ARG, "%s = %lld is out of range [1, 2^30]", names[i],
+                  (long long)dims[i]);
+  const int v = vec_elems(s->dtype);
+  if (s->d % v || s->r % v || s->d_ff % v)
+    return fail(LR_ERR_INVALID_ARG, "d, r and d_ff must be multiples of %d for this dtype", v);
+  if (s->n_panels < 1 || s->n_panels > 8)
+    return fail(LR_ERR_INVALID_ARG, "n_panels = %d is out of range [1, 8]", s->n_panels);
+  if (s->n_panels > 1) {
+    if (s->d % s->n_panels)
+      return fail(LR_ERR_INVALID_ARG, "d = %lld does not split into %d panels", (long long)s->d,
+                  s->n_panels);
+    if ((s->d / s->n_panels) % 64)
+      return fail(LR_ERR_UNSUPPORTED, "panel width %lld is not a multiple of 64",
+                  (long long)(s->d / s->n_panels));
+  }
+  if (!(s->eps >= 0.0f) || !std::isfinite(s->eps))
+    return fail(LR_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (s->emit_partials != 0 && s->emit_partials != 1)
+    return fail(LR_ERR_INVALID_ARG, "emit_partials must be 0 or 1");
+  if ((int64_t)s->T * s->d_ff > ((int64_t)1 << 40))
+    return fail(LR_ERR_UNSUPPORTED, "T * d_ff too large");
+  return LR_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(LR_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(LR_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return LR_OK;
+}
+
+#define CHECK_PTR(p)                                  \
+  do {                                                \
+    int rc_ = check_ptr((const void*)(p), #p);        \
+    if (rc_) return rc_;                              \
+  } while (0)
+
+int check_weights(const lr_block_weights* w) {
+  if (!w) return fail(LR_ERR_INVALID_ARG, "weights is NULL");
+  CHECK_PTR(w->gamma1);
+  CHECK_PTR(w->gamma2);
+  CHECK_PTR(w->A_qkv);
+  CHECK_PTR(w->B_q);
+  CHECK_PTR(w->B_k);
+  CHECK_PTR(w->B_v);
+  CHECK_PTR(w->A_o);
+  CHECK_PTR(w->B_o);
+  CHECK_PTR(w->A_gu);
+  CHECK_PTR(w->B_g);
+  CHECK_PTR(w->B_u);
+  CHECK_PTR(w->A_dn);
+  CHECK_PTR(w->B_dn);
+  return LR_OK;
+}
+
+int check_saved(const lr_block_saved* sv) {
+  if (!sv) return fail(LR_ERR_INVALID_ARG, "saved is NULL");
+  CHECK_PTR(sv->qkv_r);
+  CHECK_PTR(sv->o_r);
+  CHECK_PTR(sv->gu_r);
+  CHECK_PTR(sv->d_r);
+  CHECK_PTR(sv->rms1);
+  CHECK_PTR(sv->rms2);
+  return LR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layouts
+// ---------------------------------------------------------------------------
+struct FwdWs {
+  void *Ag_qkv, *Ag_gu, *h, *m;
+};
+
+struct BwdWs {
+  void *h, *dh, *m, *dg, *du, *dd_r, *dgus, *do_r, *dqs;
+  float *coef1, *coef2, *colpart;
+};
+
+size_t carve_fwd(const lr_block_shape* s, void* base, FwdWs* out) {
+  const size_t e = elem_size(s->dtype);
+  Carver c(base);
+  FwdWs w;
+  w.Ag_qkv = c.take(e * 3 * s->r * s->d);
+  w.Ag_gu = c.take(e * 2 * s->r * s->d);
+  w.h = c.take(e * s->T * s->d);
+  w.m = c.take(e * s->T * s->d_ff);
+  if (out) *out = w;
+  return c.off + 256;
+}
+
+size_t carve_bwd(const lr_block_shape* s, void* base, BwdWs* out) {
+  const size_t e = elem_size(s->dtype);
+  Carver c(base);
+  BwdWs w;
+  w.h = c.take(e * s->T * s->d);
+  w.dh = c.take(e * s->T * s->d);
+  w.m = c.take(e * s->T * s->d_ff);
+  w.dg = c.take(e * s->T * s->d_ff);
+  w.du = c.take(e * s->T * s->d_ff);
+  w.dd_r = c.take(e * s->T * s->r);
+  w.dgus = c.take(e * s->T * 2 * s->r);
+  w.do_r = c.take(e * s->T * s->r);
+  w.dqs = c.take(e * s->T * 3 * s->r);
+  w.coef1 = static_cast<float*>(c.take(4 * s->T));
+  w.coef2 = static_cast<float*>(c.take(4 * s->T));
+  const int bm = lr::gemm_tile_m(lr::OP_NN_RMSBWD, s->dtype);
+  const int64_t tiles = (s->T + bm - 1) / bm;
+  w.colpart = static_cast<float*>(c.take(4 * tiles * s->d));
+  if (out) *out = w;
+  return c.off + 256;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (ws_bytes < need)
+    return fail(LR_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws_bytes, need);
+  if (!ws) return fail(LR_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255u)
+    return fail(LR_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  return LR_OK;
+}
+
+// One GEMM launch with error reporting.
+int gemm(int op, int dtype, const lr::GemmDesc& d, int groups, hipStream_t st,
+         const char* what) {
+  hipError_t e = lr::run_gemm(op, dtype, d, groups, st);
+  if (e != hipSuccess) return hip_fail(e, what);
+  return LR_OK;
+}
+
+#define RUN(x)            \
+  do {                    \
+    int rc_ = (x);        \
+    if (rc_) return rc_;  \
+  } while (0)
+
+const char* B(const void* p, int64_t off_elems, size_t e) {
+  return static_cast<const char*>(p) + off_elems * e;
+}
+char* Bm(void* p, int64_t off_elems, size_t e) { return static_cast<char*>(p) + off_elems * e; }
+
+}  // namespace
+
+extern "C" {
+
+const char* lr_last_error(void) { return g_err.c_str(); }
+
+const char* lr_version(void) { return "lrblock 0.1 gfx950"; }
+
+size_t lr_block_workspace_bytes(const lr_block_shape* shape, int is_bwd) {
+  if (check_shape(shape)) return 0;
+  return is_bwd ? carve_bwd(shape, nullptr, nullptr) : carve_fwd(shape, nullptr, nullptr);
+}
+
+int lr_block_fwd(const lr_block_shape* s, const lr_block_weights* w, const void* X,
+                 const void* O_attn, void* Q, void* K, void* V, void* Y,
+                 const lr_block_saved* sv, const lr_block_partials* pt, int32_t stage, void* ws,
+                 size_t ws_bytes, void* stream) {
+  RUN(check_shape(s));
+  RUN(check_weights(w));
+  RUN(check_saved(sv));
+  if (stage < LR_STAGE_ALL || stage > LR_STAGE_POST_ATTN)
+    return fail(LR_ERR_INVALID_ARG, "stage %d is not an lr_stage", stage);
+  const bool pre = stage != LR_STAGE_POST_ATTN, post = stage != LR_STAGE_PRE_ATTN;
+  CHECK_PTR(X);
+  if (pre) {
+    CHECK_PTR(Q);
+    CHECK_PTR(K);
+    CHECK_PTR(V);
+  }
+  if (post) {
+    CHECK_PTR(O_attn);
+    CHECK_PTR(Y);
+  }
+  const bool part = s->emit_partials != 0;
+  if (part) {
+    if (!pt) return fail(LR_ERR_INVALID_ARG, "partials is NULL with emit_partials = 1");
+    if (pre) {
+      CHECK_PTR(pt->P_qkv);
+      CHECK_PTR(pt->ss1);
+    }
+    if (post) {
+      CHECK_PTR(pt->P_gu);
+      CHECK_PTR(pt->ss2);
+    }
+  }
+  const size_t need = carve_fwd(s, nullptr, nullptr);
+  RUN(check_ws(ws, ws_bytes, need));
+  FwdWs W;
+  carve_fwd(s, ws, &W);
+
+  const int dt = s->dtype;
+  const size_t e = elem_size(dt);
+  const int T = (int)s->T, d = (int)s->d, r = (int)s->r, F = (int)s->d_ff;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float inv_D = 1.0f / (float)s->d_norm;
+  // Per-panel sums of squares are written in normal mode when asked for.
+  float* ssp1 = (!part && pt && s->n_panels > 1) ? pt->ss1 : nullptr;
+  float* ssp2 = (!part && pt && s->n_panels > 1) ? pt->ss2 : nullptr;
+
+  if (pre) {
+    // Online RMSNorm + grouped [A_q; A_k; A_v] down-projection.
+    hipError_t he = lr::run_fold_gamma(dt, w->A_qkv, d, w->gamma1, W.Ag_qkv, 3 * r, d, st);
+    if (he != hipSuccess) return hip_fail(he, "fold gamma1");
+    lr::GemmDesc g;
+    g.M = T;
+    g.N = 3 * r;
+    g.K = d;
+    g.a[0] = X;
+    g.lda[0] = d;
+    g.b[0] = W.Ag_qkv;
+    g.ldb[0] = d;
+    g.c[0] = part ? pt->P_qkv : sv->qkv_r;
+    g.ldc[0] = 3 * r;
+    g.rms_out = part ? nullptr : sv->rms1;
+    g.ss_out = part ? pt->ss1 : ssp1;
+    g.n_panels = s->n_panels;
+    g.panel_width = d / s->n_panels;
+    g.inv_D = inv_D;
+    g.eps = s->eps;
+    g.emit_partial = part;
+    RUN(gemm(lr::OP_NT_ORMS, dt, g, 1, st, "QKV Online RMSNorm GEMM"));
+    if (part) {
+      he = lr::run_finalize(dt, pt->P_qkv, 3 * r, pt->ss1, T, 3 * r, inv_D, s->eps, sv->qkv_r,
+                            3 * r, sv->rms1, st);
+      if (he != hipSuccess) return hip_fail(he, "QKV finalize");
+    }
+    // Grouped Q, K, V up-projections: three (input, weight) pairs.
+    lr::GemmDesc u;
+    u.M = T;
+    u.N = d;
+    u.K = r;
+    const void* Bs[3] = {w->B_q, w->B_k, w->B_v};
+    void* Outs[3] = {Q, K, V};
+    for (int i = 0; i < 3; ++i) {
+      u.a[i] = B(sv->qkv_r, (int64_t)i * r, e);
+      u.lda[i] = 3 * r;
+      u.b[i] = Bs[i];
+      u.ldb[i] = r;
+      u.c[i] = Outs[i];
+      u.ldc[i] = d;
+    }
+    RUN(gemm(lr::OP_NT_STORE, dt, u, 3, st, "QKV grouped up-projection"));
+  }
+
+  if (post) {
+    // o_r = O A_o^T
+    lr::GemmDesc g;
+    g.M = T;
+    g.N = r;
+    g.K = d;
+    g.a[0] = O_attn;
+    g.lda[0] = d;
+    g.b[0] = w->A_o;
+    g.ldb[0] = d;
+    g.c[0] = sv->o_r;
+    g.ldc[0] = r;
+    RUN(gemm(lr::OP_NT_STORE, dt, g, 1, st, "O down-projection"));
+    // h = X + o_r B_o^T
+    lr::GemmDesc hgm;
+    hgm.M = T;
+    hgm.N = d;
+    hgm.K = r;
+    hgm.a[0] = sv->o_r;
+    hgm.lda[0] = r;
+    hgm.b[0] = w->B_o;
+    hgm.ldb[0] = r;
+    hgm.c[0] = W.h;
+    hgm.ldc[0] = d;
+    hgm.res = X;
+    hgm.ldres = d;
+    RUN(gemm(lr::OP_NT_STORE, dt, hgm, 1, st, "O up-projection + residual"));
+    // Online RMSNorm + grouped [A_g; A_u] down-projection.
+    hipError_t he = lr::run_fold_gamma(dt, w->A_gu, d, w->gamma2, W.Ag_gu, 2 * r, d, st);
+    if (he != hipSuccess) return hip_fail(he, "fold gamma2");
+    lr::GemmDesc n2;
+    n2.M = T;
+    n2.N = 2 * r;
+    n2.K = d;
+    n2.a[0] = W.h;
+    n2.lda[0] = d;
+    n2.b[0] = W.Ag_gu;
+    n2.ldb[0] = d;
+    n2.c[0] = part ? pt->P_gu : sv->gu_r;
+    n2.ldc[0] = 2 * r;
+    n2.rms_out = part ? nullptr : sv->rms2;
+    n2.ss_out = part ? pt->ss2 : ssp2;
+    n2.n_panels = s->n_panels;
+    n2.panel_width = d / s->n_panels;
+    n2.inv_D = inv_D;
+    n2.eps = s->eps;
+    n2.emit_partial = part;
+    RUN(gemm(lr::OP_NT_ORMS, dt, n2, 1, st, "gate/up Online RMSNorm GEMM"));
+    if (part) {
+      he = lr::run_finalize(dt, pt->P_gu, 2 * r, pt->ss2, T, 2 * r, inv_D, s->eps, sv->gu_r,
+                            2 * r, sv->rms2, st);
+      if (he != hipSuccess) return hip_fail(he, "gate/up finalize");
+    }
+    // m = SiLU(g_r B_g^T) * (u_r B_u^T), both pairs in one tile.
+    lr::GemmDesc sw;
+    sw.M = T;
+    sw.N = F;
+    sw.K = r;
+    sw.a[0] = sv->gu_r;
+    sw.lda[0] = 2 * r;
+    sw.b[0] = w->B_g;
+    sw.ldb[0] = r;
+    sw.a[1] = B(sv->gu_r, r, e);
+    sw.lda[1] = 2 * r;
+    sw.b[1] = w->B_u;
+    sw.ldb[1] = r;
+    sw.c[0] = W.m;
+    sw.ldc[0] = F;
+    RUN(gemm(lr::OP_NT_SWIGLU, dt, sw, 1, st, "gate/up up-projection + SwiGLU"));
+    // d_r = m A_dn^T
+    lr::GemmDesc dn;
+    dn.M = T;
+    dn.N = r;
+    dn.K = F;
+    dn.a[0] = W.m;
+    dn.lda[0] = F;
+    dn.b[0] = w->A_dn;
+    dn.ldb[0] = F;
+    dn.c[0] = sv->d_r;
+    dn.ldc[0] = r;
+    RUN(gemm(lr::OP_NT_STORE, dt, dn, 1, st, "down-projection"));
+    // Y = h + d_r B_dn^T
+    lr::GemmDesc yo;
+    yo.M = T;
+    yo.N = d;
+    yo.K = r;
+    yo.a[0] = sv->d_r;
+    yo.lda[0] = r;
+    yo.b[0] = w->B_dn;
+    yo.ldb[0] = r;
+    yo.c[0] = Y;
+    yo.ldc[0] = d;
+    yo.res = W.h;
+    yo.ldres = d;
+    RUN(gemm(lr::OP_NT_STORE, dt, yo, 1, st, "down up-projection + residual"));
+  }
+  return LR_OK;
+}
+
+int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void* X,
+                 const void* O_attn, const lr_block_saved* sv, const void* dY, const void* dQ,
+                 const void* dK, const void* dV, void* dX, void* dO_attn,
+                 const lr_block_grads* gr, int32_t stage, void* ws, size_t ws_bytes,
+                 void* stream) {
+  RUN(check_shape(s));
+  RUN(check_weights(w));
+  RUN(check_saved(sv));
+  if (!gr) return fail(LR_ERR_INVALID_ARG, "grads is NULL");
+  if (stage < LR_STAGE_ALL || stage > LR_STAGE_POST_ATTN)
+    return fail(LR_ERR_INVALID_ARG, "stage %d is not an lr_stage", stage);
+  const bool pre = stage != LR_STAGE_POST_ATTN, post = stage != LR_STAGE_PRE_ATTN;
+  CHECK_PTR(X);
+  if (post) {
+    CHECK_PTR(O_attn);
+    CHECK_PTR(dY);
+    CHECK_PTR(dO_attn);
+    CHECK_PTR(gr->gamma2);
+    CHECK_PTR(gr->A_o);
+    CHECK_PTR(gr->B_o);
+    CHECK_PTR(gr->A_gu);
+    CHECK_PTR(gr->B_g);
+    CHECK_PTR(gr->B_u);
+    CHECK_PTR(gr->A_dn);
+    CHECK_PTR(gr->B_dn);
+  }
+  if (pre) {
+    CHECK_PTR(dQ);
+    CHECK_PTR(dK);
+    CHECK_PTR(dV);
+    CHECK_PTR(dX);
+    CHECK_PTR(gr->gamma1);
+    CHECK_PTR(gr->A_qkv);
+    CHECK_PTR(gr->B_q);
+    CHECK_PTR(gr->B_k);
+    CHECK_PTR(gr->B_v);
+  }
+  const size_t need = carve_bwd(s, nullptr, nullptr);
+  RUN(check_ws(ws, ws_bytes, need));
+  BwdWs W;
+  carve_bwd(s, ws, &W);
+
+  const int dt = s->dtype;
+  const size_t e = elem_size(dt);
+  const int T = (int)s->T, d = (int)s->d, r = (int)s->r, F = (int)s->d_ff;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float inv_D = 1.0f / (float)s->d_norm;
+  const int bm_rms = lr::gemm_tile_m(lr::OP_NN_RMSBWD, dt);
+  const int tiles_rms = (T + bm_rms - 1) / bm_rms;
+
+  if (post) {
+    // dB_dn = dY^T d_r
+    {
+      lr::GemmDesc g;
+      g.M = d;
+      g.N = r;
+      g.K = T;
+      g.a[0] = dY;
+      g.lda[0] = d;
+      g.b[0] = sv->d_r;
+      g.ldb[0] = r;
+      g.c[0] = gr->B_dn;
+      g.ldc[0] = r;
+      RUN(gemm(lr::OP_TN_WGRAD, dt, g, 1, st, "dB_dn"));
+    }
+    // dd_r = dY B_dn
+    {
+      lr::GemmDesc g;
+      g.M = T;
+      g.N = r;
+      g.K = d;
+      g.a[0] = dY;
+      g.lda[0] = d;
+      g.b[0] = w->B_dn;
+      g.ldb[0] = r;
+      g.c[0] = W.dd_r;
+      g.ldc[0] = r;
+      RUN(gemm(lr::OP_NN_STORE, dt, g, 1, st, "dd_r"));
+    }
+    // Recompute g, u and dm = dd_r A_dn in one tile; m, dg, du out.
+    {
+      lr::GemmDesc g;
+      g.M = T;
+      g.N = F;
+      g.K = r;
+      g.a[0] = sv->gu_r;
+      g.lda[0] = 2 * r;
+      g.b[0] = w->B_g;
+      g.ldb[0] = r;
+      g.a[1] = B(sv->gu_r, r, e);
+      g.lda[1] = 2 * r;
+      g.b[1] = w->B_u;
+      g.ldb[1] = r;
+      g.a[2] = W.dd_r;
+      g.lda[2] = r;
+      g.b[2] = w->A_dn;
+      g.ldb[2] = F;
+      g.c[0] = W.m;
+      g.ldc[0] = F;
+      g.c[1] = W.dg;
+      g.ldc[1] = F;
+      g.c[2] = W.du;
+      g.ldc[2] = F;
+      RUN(gemm(lr::OP_SWIGLU_BWD, dt, g, 1, st, "SwiGLU recompute + backward"));
+    }
+    // dA_dn = dd_r^T m
+    {
+      lr::GemmDesc g;
+      g.M = r;
+      g.N = F;
+      g.K = T;
+      g.a[0] = W.dd_r;
+      g.lda[0] = r;
+      g.b[0] = W.m;
+      g.ldb[0] = F;
+      g.c[0] = gr->A_dn;
+      g.ldc[0] = F;
+      RUN(gemm(lr::OP_TN_WGRAD, dt, g, 1, st, "dA_dn"));
+    }
+    // dB_g = dg^T g_r, dB_u = du^T u_r (grouped)
+    {
+      lr::GemmDesc g;
+      g.M = F;
+      g.N = r;
+      g.K = T;
+      g.a[0] = W.dg;
+      g.lda[0] = F;
+      g.b[0] = sv->gu_r;
+      g.ldb[0] = 2 * r;
+      g.c[0] = gr->B_g;
+      g.ldc[0] = r;
+      g.a[1] = W.du;
+      g.lda[1] = F;
+      g.b[1] = B(sv->gu_r, r, e);
+      g.ldb[1] = 2 * r;
+      g.c[1] = gr->B_u;
+      g.ldc[1] = r;
+      RUN(gemm(lr::OP_TN_WGRAD, dt, g, 2, st, "dB_g, dB_u"));
+    }
+    // dgus = [dg B_g | du B_u] / rms2 (grouped, row-scaled)
+    {
+      lr::GemmDesc g;
+      g.M = T;
+      g.N = r;
+      g.K = F;
+      g.a[0] = W.dg;
+      g.lda[0] = F;
+      g.b[0] = w->B_g;
+      g.ldb[0] = r;
+      g.c[0] = W.dgus;
+      g.ldc[0] = 2 * r;
+      g.a[1] = W.du;
+      g.lda[1] = F;
+      g.b[1] = w->B_u;
+      g.ldb[1] = r;
+      g.c[1] = Bm(W.dgus, r, e);
+      g.ldc[1] = 2 * r;
+      g.rowdiv = sv->rms2;
+      RUN(gemm(lr::OP_NN_STORE, dt, g, 2, st, "dgu_r"));
+    }
+    // coef2 = (dgus . gu_r) / (rms2 D)
+    {
+      hipError_t he = lr::run_rowdot_coef(dt, W.dgus, 2 * r, sv->gu_r, 2 * r, 2 * r, sv->rms2,
+                                          inv_D, W.coef2, T, st);
+      if (he != hipSuccess) return hip_fail(he, "row dot 2");
+    }
+    // Recompute h = X + o_r B_o^T.
+    {
+      lr::GemmDesc g;
+      g.M = T;
+      g.N = d;
+      g.K = r;
+      g.a[0] = sv->o_r;
+      g.lda[0] = r;
+      g.b[0] = w->B_o;
+      g.ldb[0] = r;
+      g.c[0] = W.h;
+      g.ldc[0] = d;
+      g.res = X;
+      g.ldres = d;
+      RUN(gemm(lr::OP_NT_STORE, dt, g, 1, st, "recompute h"));
+    }
+    // dh = dY + gamma2 * (dgus A_gu) - coef2 * h; dgamma2 partials.
+    {
+      lr::GemmDesc g;
+      g.M = T;
+      g.N = d;
+      g.K = 2 * r;
+      g.a[0] = W.dgus;
+      g.lda[0] = 2 * r;
+      g.b[0] = w->A_gu;
+      g.ldb[0] = d;
+      g.c[0] = W.dh;
+      g.ldc[0] = d;
+      g.res = dY;
+      g.ldres = d;
+      g.hsrc = W.h;
+      g.ldh = d;
+      g.colscale = w->gamma2;
+      g.rowcoef = W.coef2;
+      g.colsum = W.colpart;
+      RUN(gemm(lr::OP_NN_RMSBWD, dt, g, 1, st, "RMSNorm-2 backward"));
+      hipError_t he = lr::run_colsum(W.colpart, tiles_rms, d, gr->gamma2, st);
+      if (he != hipSuccess) return hip_fail(he, "dgamma2");
+    }
+    // dA_gu = gamma2 * (dgus^T h)
+    {
+      lr::GemmDesc g;
+      g.M = 2 * r;
+      g.N = d;
+      g.K = T;
+      g.a[0] = W.dgus;
+      g.lda[0] = 2 * r;
+      g.b[0] = W.h;
+      g.ldb[0] = d;
+      g.c[0] = gr->A_gu;
+      g.ldc[0] = d;
+      g.colscale = w->gamma2;
+      RUN(gemm(lr::OP_TN_WGRAD, dt, g, 1, st, "dA_gu"));
+    }
+    // dB_o = dh^T o_r
+    {
+      lr::GemmDesc g;
+      g.M = d;
+      g.N = r;
+      g.K = T;
+      g.a[0] = W.dh;
+      g.lda[0] = d;
+      g.b[0] = sv->o_r;
+      g.ldb[0] = r;
+      g.c[0] = gr->B_o;
+      g.ldc[0] = r;
+      RUN(gemm(lr::OP_TN_WGRAD, dt, g, 1, st, "dB_o"));
+    }
+    // do_r = dh B_o
+    {
+      lr::GemmDesc g;
+      g.M = T;
+      g.N = r;
+      g.K = d;
+      g.a[0] = W.dh;
+      g.lda[0] = d;
+      g.b[0] = w->B_o;
+      g.ldb[0] = r;
+      g.c[0] = W.do_r;
+      g.ldc[0] = r;
+      RUN(gemm(lr::OP_NN_STORE, dt, g, 1, st, "do_r"));
+    }
+    // dA_o = do_r^T O
+    {
+      lr::GemmDesc g;
+      g.M = r;
+      g.N = d;
+      g.K = T;
+      g.a[0] = W.do_r;
+      g.lda[0] = r;
+      g.b[0] = O_attn;
+      g.ldb[0] = d;
+      g.c[0] = gr->A_o;
+      g.ldc[0] = d;
+      RUN(gemm(lr::OP_TN_WGRAD, dt, g, 1, st, "dA_o"));
+    }
+    // dO = do_r A_o
+    {
+      lr::GemmDesc g;
+      g.M = T;
+      g.N = d;
+      g.K = r;
+      g.a[0] = W.do_r;
+      g.lda[0] = r;
+      g.b[0] = w->A_o;
+      g.ldb[0] = d;
+      g.c[0] = dO_attn;
+      g.ldc[0] = d;
+      RUN(gemm(lr::OP_NN_STORE, dt, g, 1, st, "dO"));
+    }
+  }
+
+  if (pre) {
+    const void* dQKV[3] = {dQ, dK, dV};
+    const void* Bs[3] = {w->B_q, w->B_k, w->B_v};
+    float* dBs[3] = {gr->B_q, gr->B_k, gr->B_v};
+    // dB_{q,k,v} = d{Q,K,V}^T {q,k,v}_r (grouped)
+    {
+      lr::GemmDesc g;
+      g.M = d;
+      g.N = r;
+      g.K = T;
+      for (int i = 0; i < 3; ++i) {
+        g.a[i] = dQKV[i];
+        g.lda[i] = d;
+        g.b[i] = B(sv->qkv_r, (int64_t)i * r, e);
+        g.ldb[i] = 3 * r;
+        g.c[i] = dBs[i];
+        g.ldc[i] = r;
+      }
+      RUN(gemm(lr::OP_TN_WGRAD, dt, g, 3, st, "dB_q, dB_k, dB_v"));
+    }
+    // dqs = [dQ B_q | dK B_k | dV B_v] / rms1 (grouped, row-scaled)
+    {
+      lr::GemmDesc g;
+      g.M = T;
+      g.N = r;
+      g.K = d;
+      for (int i = 0; i < 3; ++i) {
+        g.a[i] = dQKV[i];
+        g.lda[i] = d;
+        g.b[i] = Bs[i];
+        g.ldb[i] = r;
+        g.c[i] = Bm(W.dqs, (int64_t)i * r, e);
+        g.ldc[i] = 3 * r;
+      }
+      g.rowdiv = sv->rms1;
+      RUN(gemm(lr::OP_NN_STORE, dt, g, 3, st, "dqkv_r"));
+    }
+    // coef1 = (dqs . qkv_r) / (rms1 D)
+    {
+      hipError_t he = lr::run_rowdot_coef(dt, W.dqs, 3 * r, sv->qkv_r, 3 * r, 3 * r, sv->rms1,
+                                          inv_D, W.coef1, T, st);
+      if (he != hipSuccess) return hip_fail(he, "row dot 1");
+    }
+    // dX = dh + gamma1 * (dqs A_qkv) - coef1 * X; dgamma1 partials.
+    {
+      lr::GemmDesc g;
+      g.M = T;
+      g.N = d;
+      g.K = 3 * r;
+      g.a[0] = W.dqs;
+      g.lda[0] = 3 * r;
+      g.b[0] = w->A_qkv;
+      g.ldb[0] = d;
+      g.c[0] = dX;
+      g.ldc[0] = d;
+      g.res = W.dh;
+      g.ldres = d;
+      g.hsrc = X;
+      g.ldh = d;
+      g.colscale = w->gamma1;
+      g.rowcoef = W.coef1;
+      g.colsum = W.colpart;
+      RUN(gemm(lr::OP_NN_RMSBWD, dt, g, 1, st, "RMSNorm-1 backward"));
+      hipError_t he = lr::run_colsum(W.colpart, tiles_rms, d, gr->gamma1, st);
+      if (he != hipSuccess) return hip_fail(he, "dgamma1");
+    }
+    // dA_qkv = gamma1 * (dqs^T X)
+    {
+      lr::GemmDesc g;
+      g.M = 3 * r;
+      g.N = d;
+      g.K = T;
+      g.a[0] = W.dqs;
+      g.lda[0] = 3 * r;
+      g.b[0] = X;
+      g.ldb[0] = d;
+      g.c[0] = gr->A_qkv;
+      g.ldc[0] = d;
+      g.colscale = w->gamma1;
+      RUN(gemm(lr::OP_TN_WGRAD, dt, g, 1, st, "dA_qkv"));
+    }
+  }
+  return LR_OK;
+}
+
+int lr_grouped_lowrank_gemm(int32_t G, const lr_gemm_pair* pairs, int32_t dtype, int32_t layout,
+                            int32_t epilogue, void* stream) {
+  if (dtype != LR_F32 && dtype != LR_BF16)
+    return fail(LR_ERR_INVALID_ARG, "dtype %d is neither LR_F32 nor LR_BF16", dtype);
+  if (G < 1 || G > 3) return fail(LR_ERR_INVALID_ARG, "G = %d is out of range [1, 3]", G);
+  if (!pairs) return fail(LR_ERR_INVALID_ARG, "pairs is NULL");
+  if (layout < LR_LAYOUT_NT || layout > LR_LAYOUT_TN)
+    return fail(LR_ERR_INVALID_ARG, "layout %d is not an lr_layout", layout);
+  if (epilogue < LR_EPI_NONE || epilogue > LR_EPI_ROW_SCALE)
+    return fail(LR_ERR_INVALID_ARG, "epilogue %d is not an lr_epilogue", epilogue);
+  const int v = vec_elems(dtype);
+  const lr_gemm_pair& p0 = pairs[0];
+  for (int i = 0; i < G; ++i) {
+    const lr_gemm_pair& p = pairs[i];
+    if (p.M < 1 || p.N < 1 || p.K < 1 || p.M > kMaxDim || p.N > kMaxDim || p.K > kMaxDim)
+      return fail(LR_ERR_INVALID_ARG, "pair %d: M, N, K must be in [1, 2^30]", i);
+    if (p.M != p0.M || p.N != p0.N || p.K != p0.K)
+      return fail(LR_ERR_UNSUPPORTED, "pair %d: all pairs of a call must have equal M, N, K", i);
+    if (check_ptr(p.X, "X") || check_ptr(p.W, "W") || check_ptr(p.Y, "Y"))
+      return fail(LR_ERR_INVALID_ARG, "pair %d: %s", i, g_err.c_str());
+    const int64_t minx = layout == LR_LAYOUT_TN ? p.M : p.K;
+    const int64_t minw = layout == LR_LAYOUT_NT ? p.K : p.N;
+    if (p.ldx < minx || p.ldw < minw || p.ldy < p.N)
+      return fail(LR_ERR_INVALID_ARG, "pair %d: leading dimension smaller than the row", i);
+    if (p.ldx % v || p.ldw % v || p.ldy % v)
+      return fail(LR_ERR_INVALID_ARG, "pair %d: leading dimensions must be multiples of %d", i,
+                  v);
+    if (epilogue == LR_EPI_ADD_RESIDUAL) {
+      if (check_ptr(p.aux, "aux")) return fail(LR_ERR_INVALID_ARG, "pair %d: %s", i, g_err.c_str());
+      if (p.ldaux < p.N || p.ldaux % v)
+        return fail(LR_ERR_INVALID_ARG, "pair %d: bad residual leading dimension", i);
+    }
+    if (epilogue == LR_EPI_ROW_SCALE && !p.aux)
+      return fail(LR_ERR_INVALID_ARG, "pair %d: row scale aux is NULL", i);
+  }
+  if (layout == LR_LAYOUT_TN && epilogue != LR_EPI_NONE)
+    return fail(LR_ERR_UNSUPPORTED, "the TN layout takes no epilogue");
+  if (epilogue == LR_EPI_SWIGLU_PAIR && (G != 2 || layout != LR_LAYOUT_NT))
+    return fail(LR_ERR_UNSUPPORTED, "LR_EPI_SWIGLU_PAIR needs G = 2 and the NT layout");
+  if ((epilogue == LR_EPI_ADD_RESIDUAL || epilogue == LR_EPI_ROW_SCALE) && G > 1) {
+    for (int i = 1; i < G; ++i)
+      if (pairs[i].aux != p0.aux || pairs[i].ldaux != p0.ldaux)
+        return fail(LR_ERR_UNSUPPORTED, "grouped epilogue inputs must be shared by all pairs");
+    if (epilogue == LR_EPI_ADD_RESIDUAL)
+      return fail(LR_ERR_UNSUPPORTED, "the residual epilogue takes G = 1");
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  lr::GemmDesc g;
+  g.M = (int)p0.M;
+  g.N = (int)p0.N;
+  g.K = (int)p0.K;
+  for (int i = 0; i < G; ++i) {
+    g.a[i] = pairs[i].X;
+    g.lda[i] = pairs[i].ldx;
+    g.b[i] = pairs[i].W;
+    g.ldb[i] = pairs[i].ldw;
+    g.c[i] = pairs[i].Y;
+    g.ldc[i] = pairs[i].ldy;
+  }
+  if (epilogue == LR_EPI_ADD_RESIDUAL) {
+    g.res = p0.aux;
+    g.ldres = p0.ldaux;
+  } else if (epilogue == LR_EPI_ROW_SCALE) {
+    g.rowdiv = static_cast<const float*>(p0.aux);
+  }
+  int op;
+  int groups = G;
+  if (epilogue == LR_EPI_SWIGLU_PAIR) {
+    op = lr::OP_NT_SWIGLU;
+    groups = 1;
+  } else if (layout == LR_LAYOUT_NT) {
+    op = lr::OP_NT_STORE;
+  } else if (layout == LR_LAYOUT_NN) {
+    op = lr::OP_NN_STORE;
+  } else {
+    op = lr::OP_TN_WGRAD;
+  }
+  return gemm(op, dtype, g, groups, st, "grouped low-rank GEMM");
+}
+
+size_t lr_online_rmsnorm_gemm_workspace_bytes(int64_t N, int64_t d, int32_t dtype) {
+  if ((dtype != LR_F32 && dtype != LR_BF16) || N < 1 || d < 1) return 0;
+  return (size_t)N * (size_t)d * elem_size(dtype);
+}
+
+int lr_online_rmsnorm_gemm(int64_t T, int64_t d, int64_t N, int32_t n_panels, int64_t d_norm,
+                           float eps, const void* X, int64_t ldx, const void* gamma,
+                           const void* A, int64_t lda, void* out, int64_t ldo, float* rms_out,
+                           float* ss_out, int32_t emit_partial, int32_t dtype, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (dtype != LR_F32 && dtype != LR_BF16)
+    return fail(LR_ERR_INVALID_ARG, "dtype %d is neither LR_F32 nor LR_BF16", dtype);
+  if (T < 1 || d < 1 || N < 1 || d_norm < 1 || T > kMaxDim || d > kMaxDim || N > kMaxDim ||
+      d_norm > kMaxDim)
+    return fail(LR_ERR_INVALID_ARG, "T, d, N, d_norm must be in [1, 2^30]");
+  const int v = vec_elems(dtype);
+  if (d % v) return fail(LR_ERR_INVALID_ARG, "d must be a multiple of %d for this dtype", v);
+  if (ldx < d || lda < d || ldo < N || ldx % v || lda % v || ldo % v)
+    return fail(LR_ERR_INVALID_ARG, "leading dimensions must cover the row and be multiples of %d",
+                v);
+  if (n_panels < 1 || n_panels > 8)
+    return fail(LR_ERR_INVALID_ARG, "n_panels = %d is out of range [1, 8]", n_panels);
+  if (n_panels > 1 && (d % n_panels || (d / n_panels) % 64))
+    return fail(d % n_panels ? LR_ERR_INVALID_ARG : LR_ERR_UNSUPPORTED,
+                "d = %lld does not split into %d panels of a multiple of 64 columns",
+                (long long)d, n_panels);
+  if (!(eps >= 0.0f) || !std::isfinite(eps))
+    return fail(LR_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (emit_partial != 0 && emit_partial != 1)
+    return fail(LR_ERR_INVALID_ARG, "emit_partial must be 0 or 1");
+  CHECK_PTR(X);
+  CHECK_PTR(A);
+  CHECK_PTR(out);
+  if (gamma) CHECK_PTR(gamma);
+  if (rms_out && (reinterpret_cast<uintptr_t>(rms_out) & 3u))
+    return fail(LR_ERR_INVALID_ARG, "rms_out is not 4-byte aligned");
+  if (ss_out && (reinterpret_cast<uintptr_t>(ss_out) & 3u))
+    return fail(LR_ERR_INVALID_ARG, "ss_out is not 4-byte aligned");
+  const void* Aeff = A;
+  int64_t ldaeff = lda;
+  if (gamma) {
+    const size_t need = (size_t)N * (size_t)d * elem_size(dtype);
+    if (ws_bytes < need || !ws)
+      return fail(LR_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                  ws_bytes, need);
+    if (!aligned16(ws)) return fail(LR_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (gamma) {
+    hipError_t he = lr::run_fold_gamma(dtype, A, lda, gamma, ws, (int)N, (int)d, st);
+    if (he != hipSuccess) return hip_fail(he, "fold gamma");
+    Aeff = ws;
+    ldaeff = d;
+  }
+  lr::GemmDesc g;
+  g.M = (int)T;
+  g.N = (int)N;
+  g.K = (int)d;
+  g.a[0] = X;
+  g.lda[0] = ldx;
+  g.b[0] = Aeff;
+  g.ldb[0] = ldaeff;
+  g.c[0] = out;
+  g.ldc[0] = ldo;
+  g.rms_out = emit_partial ? nullptr : rms_out;
+  g.ss_out = ss_out;
+  g.n_panels = n_panels;
+  g.panel_width = (int)(d / n_panels);
+  g.inv_D = 1.0f / (float)d_norm;
+  g.eps = eps;
+  g.emit_partial = emit_partial;
+  return gemm(lr::OP_NT_ORMS, dtype, g, 1, st, "Online RMSNorm GEMM");
+}
+
+}  // extern "C"

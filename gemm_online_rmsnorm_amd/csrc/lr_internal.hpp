@@ -1,0 +1,66 @@
+// Internal launch interface between the C ABI (lr_api.cpp) and the kernels
+// (lr_kernels.hip). Host-only declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lr {
+
+// GEMM operations (layout + epilogue); see lr_gemm.hpp for the epilogues.
+enum GemmOp : int {
+  OP_NT_STORE = 0,    // Y = X W^T [/ rowdiv] [+ res]           (grouped)
+  OP_NT_ORMS = 1,     // Online RMSNorm down-projection
+  OP_NT_SWIGLU = 2,   // two NT pairs, Y = SiLU(acc0) * acc1
+  OP_SWIGLU_BWD = 3,  // NT, NT, NN pairs -> m, dg, du
+  OP_NN_STORE = 4,    // Y = X W [/ rowdiv] [+ res]             (grouped)
+  OP_NN_RMSBWD = 5,   // RMSNorm backward epilogue + column sums
+  OP_TN_WGRAD = 6,    // fp32 Y = X^T W [* colscale]            (grouped)
+  OP_COUNT = 7,
+};
+
+struct GemmDesc {
+  int M = 0, N = 0, K = 0;
+  const void* a[3] = {nullptr, nullptr, nullptr};
+  int64_t lda[3] = {0, 0, 0};
+  const void* b[3] = {nullptr, nullptr, nullptr};
+  int64_t ldb[3] = {0, 0, 0};
+  void* c[3] = {nullptr, nullptr, nullptr};
+  int64_t ldc[3] = {0, 0, 0};
+  const void* res = nullptr;
+  int64_t ldres = 0;
+  const void* hsrc = nullptr;
+  int64_t ldh = 0;
+  const float* rowdiv = nullptr;
+  const float* rowcoef = nullptr;
+  const void* colscale = nullptr;
+  float* colsum = nullptr;
+  float* rms_out = nullptr;
+  float* ss_out = nullptr;
+  int n_panels = 1;
+  int panel_width = 0;  // columns per Online RMSNorm panel
+  float inv_D = 0.f;
+  float eps = 0.f;
+  int emit_partial = 0;
+};
+
+// Tile sizes an operation uses for a dtype (0 = LR_F32, 1 = LR_BF16).
+int gemm_tile_m(int op, int dtype);
+int gemm_tile_k(int op, int dtype);
+
+// Enqueue one GEMM launch over `groups` operand groups (grid z).
+hipError_t run_gemm(int op, int dtype, const GemmDesc& d, int groups, hipStream_t s);
+
+// Memory-bound helpers.
+hipError_t run_fold_gamma(int dtype, const void* A, int64_t lda, const void* gamma, void* out,
+                          int rows, int cols, hipStream_t s);
+hipError_t run_rowdot_coef(int dtype, const void* a, int64_t lda, const void* b, int64_t ldb,
+                           int width, const float* rms, float inv_D, float* coef, int rows,
+                           hipStream_t s);
+hipError_t run_colsum(const float* part, int tiles, int n, float* out, hipStream_t s);
+hipError_t run_finalize(int dtype, const void* P, int64_t ldp, const float* ss, int rows,
+                        int width, float inv_D, float eps, void* z, int64_t ldz, float* rms_out,
+                        hipStream_t s);
+
+}  // namespace lr

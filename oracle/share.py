@@ -58,6 +58,14 @@ def shard_weights(W, k: int, i: int):
     return Wi, S, SF
 
 
+def norm_chunk_payload(gamma, x, A):
+    """All-reduce payload of a norm chunk on one rank: the partial product of
+    the gamma-scaled (not yet normalised) slice, (gamma * x) A^T, and the
+    slice's per-row sum of squares (project page, "Three supporting changes",
+    Online RMSNorm: the sum of squares travels with the chunk's all-reduce)."""
+    return (gamma[None, :] * x) @ A.T, np.sum(x * x, axis=1)
+
+
 def _forward_steps(Wi, Xi, Oi, D: int, eps: float):
     r = Wi["A_q"].shape[0]
     A_qkv = np.concatenate([Wi["A_q"], Wi["A_k"], Wi["A_v"]], axis=0)
@@ -65,8 +73,7 @@ def _forward_steps(Wi, Xi, Oi, D: int, eps: float):
     out = {}
     # Chunk ending at the grouped QKV down-projection: partial product of the
     # un-normalised (gamma-scaled) slice plus the slice's sum of squares.
-    P_qkv = (Wi["gamma1"][None, :] * Xi) @ A_qkv.T
-    ss1 = np.sum(Xi * Xi, axis=1)
+    P_qkv, ss1 = norm_chunk_payload(Wi["gamma1"], Xi, A_qkv)
     out["P_qkv"], out["ss1"] = P_qkv, ss1
     P_qkv_red, ss1_red = yield (P_qkv, ss1)
     rms1 = np.sqrt(ss1_red / D + eps)
@@ -80,8 +87,7 @@ def _forward_steps(Wi, Xi, Oi, D: int, eps: float):
     (o_r,) = yield (P_o,)
     # Chunk from B_o through the residual and Online RMSNorm to A_gu.
     h = Xi + o_r @ Wi["B_o"].T
-    P_gu = (Wi["gamma2"][None, :] * h) @ A_gu.T
-    ss2 = np.sum(h * h, axis=1)
+    P_gu, ss2 = norm_chunk_payload(Wi["gamma2"], h, A_gu)
     out["P_gu"], out["ss2"] = P_gu, ss2
     P_gu_red, ss2_red = yield (P_gu, ss2)
     rms2 = np.sqrt(ss2_red / D + eps)
