@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Benchmark of the low-rank decoder-block linear stack on one MI355X.
+
+One step = the block's forward and backward (lr_block_fwd + lr_block_bwd)
+over one batch of 16384 synthetic tokens, with every input already resident
+in HBM. Prints ONE JSON line:
+  value          tokens/s of fwd+bwd (T / step time)
+  tflops         algorithmic TFLOP/s including the mandated recompute
+  roofline       the dominant kernel against the bf16 MFMA peak, from HIP
+                 events recorded around its launches on its stream
+  cpu_baseline   the fp64 CPU oracle on a bounded sample of the same
+                 workload, on this host's cores
+
+    python bench.py [--steps 8] [--warmup 2] [--config 3]
+
+The default workload is the 7B-shape block (d = 4096, r = 1024,
+d_ff = 11008); the other workloads are parity-test cases.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+MFMA_FP32_PEAK_TFLOPS = 157.3    # MI355X dense fp32
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=8)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: 7B shape)")
+    ap.add_argument("--cpu-rows", type=int, default=6144,
+                    help="tokens of the workload the CPU oracle runs for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernels", action="store_true", help="also print the per-kernel table")
+    return ap.parse_args()
+
+
+def cpu_baseline(s, inputs, rows):
+    """The oracle as it stands, timed on a bounded sample of the workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    rows = min(rows, s.T)
+    sample = {k: (v[:rows] if v.shape[0] == s.T and k in ("X", "O", "dY", "dQ", "dK", "dV")
+                  else v) for k, v in inputs.items()}
+    t0 = time.perf_counter()
+    out = oracle.run_fwd_bwd(sample, D=s.D, eps=s.eps, n_panels=s.P, partials=s.partials,
+                             row_block=2048)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(out["dA_qkv"]).all()
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"first {rows} of {s.T} tokens of the {s.name} workload, full fwd+bwd "
+                      f"incl. weight grads, numpy float64 (OpenBLAS)"}
+
+
+def main():
+    args = _parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU's share of the block; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported: collectives and multi-GPU runs are "
+              "outside this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import gemm_online_rmsnorm_amd as lr
+    from gemm_online_rmsnorm_amd.runner import BlockRun
+    from gemm_online_rmsnorm_amd.work import MEMORY_BOUND, kernel_work
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lr._lib.load()
+    s = synth.config(args.config)
+    print(f"[bench] workload {s.name} T={s.T} d={s.d} r={s.r} F={s.F} D={s.D} P={s.P}",
+          file=sys.stderr, flush=True)
+    inputs = synth.make_inputs(s)
+    run = BlockRun(s.T, s.d, s.r, s.F, s.D, s.P, s.dtype, s.eps, s.partials, inputs,
+                   heads=s.heads)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        run.step(stream)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps between two events on the stream the library uses.
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        run.step(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # Per-kernel pass: the library brackets each launch with HIP events on
+    # its stream; same K steps again.
+    lr.profile_enable(True)
+    for _ in range(args.steps):
+        run.step(stream)
+    torch.cuda.synchronize()
+    lr.profile_enable(False)
+    prof = lr.profile_collect()
+    elem = 2 if s.dtype == "bf16" else 4
+    work = kernel_work(s.T, s.d, s.r, s.F, elem, s.partials, s.P)
+    kernels = []
+    for name, count, total in prof:
+        per = total / count
+        fl, by = work.get(name, (0.0, 0.0))
+        kernels.append({
+            "kernel": name, "launches_per_step": count // args.steps,
+            "ms": round(per, 4),
+            "tflops": round(fl / (per * 1e-3) / 1e12, 1) if fl else None,
+            "gbs": round(by / (per * 1e-3) / 1e9, 1),
+            "bound": "hbm" if name in MEMORY_BOUND else "mfma",
+            "step_ms": round(total / args.steps, 4),
+        })
+    kernel_ms = sum(k["step_ms"] for k in kernels)
+    dom = max(kernels, key=lambda k: k["step_ms"])
+    peak = MFMA_BF16_PEAK_TFLOPS if s.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    roofline = {
+        "kernel": dom["kernel"],
+        "bound": dom["bound"],
+        "achieved": dom["tflops"] if dom["bound"] == "mfma" else dom["gbs"],
+        "peak": peak if dom["bound"] == "mfma" else HBM_PEAK_GBS,
+        "unit": "TFLOP/s" if dom["bound"] == "mfma" else "GB/s",
+        "traffic": None,
+        "ms_per_launch": dom["ms"],
+    }
+    roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
+
+    flop_step = s.T * (s.fwd_flop_per_token() + s.bwd_flop_per_token()
+                       + s.recompute_flop_per_token())
+    flop_model = s.T * 3 * s.fwd_flop_per_token()
+    tflops = flop_step / (ms * 1e-3) / 1e12
+    mem = [k for k in kernels if k["bound"] == "hbm" and k["kernel"].startswith("row dot")]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu_baseline: timing the fp64 oracle on a sample", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(s, inputs, args.cpu_rows)
+
+    line = {
+        "metric": "fwd+bwd low-rank block tokens/s + TFLOP/s as % of MI355X bf16 MFMA peak",
+        "value": round(s.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic (seeded Gaussian inputs and random-init factors of the workload's shapes)",
+        "config": {"workload": f"{s.name} low-rank decoder-block linear stack, fwd+bwd",
+                   "tokens": s.T, "d": s.d, "r": s.r, "d_ff": s.F, "d_norm": s.D,
+                   "n_panels": s.P, "rank_share": s.partials},
+        "tflops": round(tflops, 1),
+        "tflops_model": round(flop_model / (ms * 1e-3) / 1e12, 1),
+        "mfma_peak_frac": round(tflops / peak, 4),
+        "roofline": roofline,
+        "rowdot_hbm": [{"kernel": k["kernel"], "gbs": k["gbs"],
+                        "frac": round(k["gbs"] / HBM_PEAK_GBS, 3)} for k in mem],
+        "kernel_ms_sum": round(kernel_ms, 4),
+        "wall_s": round(wall, 3),
+        "cpu_baseline": cpu,
+    }
+    if args.kernels:
+        for k in sorted(kernels, key=lambda k: -k["step_ms"]):
+            print(json.dumps(k), file=sys.stderr)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

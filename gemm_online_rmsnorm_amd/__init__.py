@@ -140,5 +140,21 @@ def online_rmsnorm_gemm(X, gamma, A, out, *, n_panels=1, d_norm=None, eps=1e-5, 
         _stream(stream, X.device)))
 
 
+def profile_enable(on: bool = True) -> None:
+    """Start (True) or stop (False) per-kernel HIP-event timing in the library."""
+    _lib.check(_lib.load().lr_profile_enable(int(bool(on))))
+
+
+def profile_collect(max_kernels: int = 64) -> list[tuple[str, int, float]]:
+    """Wait for the recorded events; return [(kernel, launches, total ms)]."""
+    lib = _lib.load()
+    arr = (_lib.lr_kernel_time * max_kernels)()
+    n = lib.lr_profile_collect(arr, max_kernels)
+    if n < 0:
+        _lib.check(n)
+    return [(arr[i].name.decode(), int(arr[i].count), float(arr[i].total_ms))
+            for i in range(min(n, max_kernels))]
+
+
 def version() -> str:
     return _lib.load().lr_version().decode()

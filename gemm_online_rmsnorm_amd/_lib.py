@@ -29,7 +29,8 @@ LR_EPI_NONE, LR_EPI_ADD_RESIDUAL, LR_EPI_SWIGLU_PAIR, LR_EPI_ROW_SCALE = 0, 1, 2
 EXPORTS = (
     "lr_block_workspace_bytes", "lr_block_fwd", "lr_block_bwd",
     "lr_grouped_lowrank_gemm", "lr_online_rmsnorm_gemm_workspace_bytes",
-    "lr_online_rmsnorm_gemm", "lr_last_error", "lr_version",
+    "lr_online_rmsnorm_gemm", "lr_profile_enable", "lr_profile_collect", "lr_last_error",
+    "lr_version",
 )
 
 
@@ -57,6 +58,10 @@ class lr_block_grads(ctypes.Structure):
 
 class lr_block_partials(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("P_qkv", "P_gu", "ss1", "ss2")]
+
+
+class lr_kernel_time(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 64), ("count", c_int32), ("total_ms", c_float)]
 
 
 class lr_gemm_pair(ctypes.Structure):
@@ -100,6 +105,10 @@ def load(path: str | None = None):
         c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
         c_size_t, c_void_p]
     lib.lr_online_rmsnorm_gemm.restype = c_int32
+    lib.lr_profile_enable.argtypes = [c_int32]
+    lib.lr_profile_enable.restype = c_int32
+    lib.lr_profile_collect.argtypes = [POINTER(lr_kernel_time), c_int32]
+    lib.lr_profile_collect.restype = c_int32
     lib.lr_last_error.argtypes = []
     lib.lr_last_error.restype = ctypes.c_char_p
     lib.lr_version.argtypes = []

@@ -6,11 +6,14 @@
 // made, so argument errors are reported identically on hosts without a GPU.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/lr_block.h"
 #include "lr_internal.hpp"
@@ -38,6 +41,49 @@ int hip_fail(hipError_t e, const char* what) {
     hipError_t e_ = (call);                       \
     if (e_ != hipSuccess) return hip_fail(e_, what); \
   } while (0)
+
+// ---------------------------------------------------------------------------
+// Measurement hook: HIP events around each launch while enabled.
+// ---------------------------------------------------------------------------
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+std::atomic<bool> g_prof_on{false};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records a start event on construction and a stop event on destruction.
+struct ProfScope {
+  hipStream_t s;
+  size_t idx = SIZE_MAX;
+  ProfScope(const char* name, hipStream_t st) : s(st) {
+    if (!g_prof_on.load(std::memory_order_relaxed)) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    ProfRec r{name, prof_event(), prof_event()};
+    if (!r.a || !r.b) return;
+    (void)hipEventRecord(r.a, s);
+    idx = g_prof.size();
+    g_prof.push_back(r);
+  }
+  ~ProfScope() {
+    if (idx == SIZE_MAX) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    (void)hipEventRecord(g_prof[idx].b, s);
+  }
+};
 
 size_t elem_size(int dtype) { return dtype == LR_F32 ? 4 : 2; }
 int vec_elems(int dtype) { return dtype == LR_F32 ? 4 : 8; }
@@ -191,6 +237,7 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
 // One GEMM launch with error reporting.
 int gemm(int op, int dtype, const lr::GemmDesc& d, int groups, hipStream_t st,
          const char* what) {
+  ProfScope ps(what, st);
   hipError_t e = lr::run_gemm(op, dtype, d, groups, st);
   if (e != hipSuccess) return hip_fail(e, what);
   return LR_OK;
@@ -214,6 +261,51 @@ extern "C" {
 const char* lr_last_error(void) { return g_err.c_str(); }
 
 const char* lr_version(void) { return "lrblock 0.1 gfx950"; }
+
+int lr_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (on) {
+    for (auto& r : g_prof) {
+      g_prof_pool.push_back(r.a);
+      g_prof_pool.push_back(r.b);
+    }
+    g_prof.clear();
+  }
+  g_prof_on.store(on != 0);
+  return LR_OK;
+}
+
+int lr_profile_collect(lr_kernel_time* out, int32_t max) {
+  if (max < 0 || (max > 0 && !out)) return fail(LR_ERR_INVALID_ARG, "bad output array");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  struct Agg {
+    const char* name;
+    int count;
+    double ms;
+  };
+  std::vector<Agg> agg;
+  for (auto& r : g_prof) {
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return hip_fail(e, "profile event");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "profile elapsed time");
+    size_t i = 0;
+    while (i < agg.size() && std::strcmp(agg[i].name, r.name) != 0) ++i;
+    if (i == agg.size()) agg.push_back({r.name, 0, 0.0});
+    agg[i].count += 1;
+    agg[i].ms += ms;
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof.clear();
+  for (size_t i = 0; i < agg.size() && (int)i < max; ++i) {
+    std::snprintf(out[i].name, sizeof(out[i].name), "%s", agg[i].name);
+    out[i].count = agg[i].count;
+    out[i].total_ms = (float)agg[i].ms;
+  }
+  return (int)agg.size();
+}
 
 size_t lr_block_workspace_bytes(const lr_block_shape* shape, int is_bwd) {
   if (check_shape(shape)) return 0;
@@ -268,7 +360,11 @@ int lr_block_fwd(const lr_block_shape* s, const lr_block_weights* w, const void*
 
   if (pre) {
     // Online RMSNorm + grouped [A_q; A_k; A_v] down-projection.
-    hipError_t he = lr::run_fold_gamma(dt, w->A_qkv, d, w->gamma1, W.Ag_qkv, 3 * r, d, st);
+    hipError_t he;
+    {
+      ProfScope ps("fold gamma1", st);
+      he = lr::run_fold_gamma(dt, w->A_qkv, d, w->gamma1, W.Ag_qkv, 3 * r, d, st);
+    }
     if (he != hipSuccess) return hip_fail(he, "fold gamma1");
     lr::GemmDesc g;
     g.M = T;
@@ -289,6 +385,7 @@ int lr_block_fwd(const lr_block_shape* s, const lr_block_weights* w, const void*
     g.emit_partial = part;
     RUN(gemm(lr::OP_NT_ORMS, dt, g, 1, st, "QKV Online RMSNorm GEMM"));
     if (part) {
+      ProfScope ps("QKV finalize", st);
       he = lr::run_finalize(dt, pt->P_qkv, 3 * r, pt->ss1, T, 3 * r, inv_D, s->eps, sv->qkv_r,
                             3 * r, sv->rms1, st);
       if (he != hipSuccess) return hip_fail(he, "QKV finalize");
@@ -339,7 +436,11 @@ int lr_block_fwd(const lr_block_shape* s, const lr_block_weights* w, const void*
     hgm.ldres = d;
     RUN(gemm(lr::OP_NT_STORE, dt, hgm, 1, st, "O up-projection + residual"));
     // Online RMSNorm + grouped [A_g; A_u] down-projection.
-    hipError_t he = lr::run_fold_gamma(dt, w->A_gu, d, w->gamma2, W.Ag_gu, 2 * r, d, st);
+    hipError_t he;
+    {
+      ProfScope ps("fold gamma2", st);
+      he = lr::run_fold_gamma(dt, w->A_gu, d, w->gamma2, W.Ag_gu, 2 * r, d, st);
+    }
     if (he != hipSuccess) return hip_fail(he, "fold gamma2");
     lr::GemmDesc n2;
     n2.M = T;
@@ -360,6 +461,7 @@ int lr_block_fwd(const lr_block_shape* s, const lr_block_weights* w, const void*
     n2.emit_partial = part;
     RUN(gemm(lr::OP_NT_ORMS, dt, n2, 1, st, "gate/up Online RMSNorm GEMM"));
     if (part) {
+      ProfScope ps("gate/up finalize", st);
       he = lr::run_finalize(dt, pt->P_gu, 2 * r, pt->ss2, T, 2 * r, inv_D, s->eps, sv->gu_r,
                             2 * r, sv->rms2, st);
       if (he != hipSuccess) return hip_fail(he, "gate/up finalize");
@@ -572,6 +674,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
     }
     // coef2 = (dgus . gu_r) / (rms2 D)
     {
+      ProfScope ps("row dot 2", st);
       hipError_t he = lr::run_rowdot_coef(dt, W.dgus, 2 * r, sv->gu_r, 2 * r, 2 * r, sv->rms2,
                                           inv_D, W.coef2, T, st);
       if (he != hipSuccess) return hip_fail(he, "row dot 2");
@@ -612,6 +715,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.rowcoef = W.coef2;
       g.colsum = W.colpart;
       RUN(gemm(lr::OP_NN_RMSBWD, dt, g, 1, st, "RMSNorm-2 backward"));
+      ProfScope ps("dgamma2 column sum", st);
       hipError_t he = lr::run_colsum(W.colpart, tiles_rms, d, gr->gamma2, st);
       if (he != hipSuccess) return hip_fail(he, "dgamma2");
     }
@@ -727,6 +831,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
     }
     // coef1 = (dqs . qkv_r) / (rms1 D)
     {
+      ProfScope ps("row dot 1", st);
       hipError_t he = lr::run_rowdot_coef(dt, W.dqs, 3 * r, sv->qkv_r, 3 * r, 3 * r, sv->rms1,
                                           inv_D, W.coef1, T, st);
       if (he != hipSuccess) return hip_fail(he, "row dot 1");
@@ -751,6 +856,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.rowcoef = W.coef1;
       g.colsum = W.colpart;
       RUN(gemm(lr::OP_NN_RMSBWD, dt, g, 1, st, "RMSNorm-1 backward"));
+      ProfScope ps("dgamma1 column sum", st);
       hipError_t he = lr::run_colsum(W.colpart, tiles_rms, d, gr->gamma1, st);
       if (he != hipSuccess) return hip_fail(he, "dgamma1");
     }

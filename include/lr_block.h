@@ -134,7 +134,10 @@ typedef struct {
  * (in `dtype`) are the unreduced payloads (gamma * x) A^T of the two norm
  * chunks and ss1, ss2 [T] (fp32) the sums of squares of this GPU's slice of
  * X and h that travel with them. The payloads of the other two chunks are
- * o_r and d_r themselves (lr_block_saved). */
+ * o_r and d_r themselves (lr_block_saved). In normal mode (emit_partials =
+ * 0) with n_panels > 1 the struct is optional: non-NULL ss1, ss2 then
+ * receive the per-panel sums of squares [P, T] of X and h, and P_qkv, P_gu
+ * are ignored. */
 typedef struct {
   void *P_qkv, *P_gu;
   float *ss1, *ss2;
@@ -152,8 +155,8 @@ size_t lr_block_workspace_bytes(const lr_block_shape* shape, int is_bwd);
  *   Q, K, V [T, d]  outputs for the attention core (PRE_ATTN and ALL)
  *   Y [T, d]        block output (POST_ATTN and ALL)
  *   saved           outputs kept for the backward
- *   partials        required when shape->emit_partials, else ignored (may
- *                   be NULL)
+ *   partials        required when shape->emit_partials; otherwise NULL or
+ *                   the per-panel statistics outputs (see lr_block_partials)
  *   ws, ws_bytes    workspace of lr_block_workspace_bytes(shape, 0) bytes
  * Steps: Online RMSNorm of X fused into the grouped QKV down-projection
  * (per-row sums of squares accumulated per K-panel from the staged X tiles,
@@ -245,6 +248,24 @@ int lr_online_rmsnorm_gemm(int64_t T, int64_t d, int64_t N, int32_t n_panels, in
                            const void* A, int64_t lda, void* out, int64_t ldo, float* rms_out,
                            float* ss_out, int32_t emit_partial, int32_t dtype, void* ws,
                            size_t ws_bytes, void* stream);
+
+/* Measurement hook. While enabled, every kernel the library enqueues is
+ * bracketed by a pair of HIP events recorded on the stream it is launched on
+ * (events are created on first use and reused; no device memory is
+ * allocated). lr_profile_enable(1) starts a new recording, (0) stops it.
+ * lr_profile_collect waits for the recorded events, writes up to `max`
+ * per-kernel aggregates (name, launch count, summed milliseconds) in order
+ * of first launch, clears the recording and returns the number of distinct
+ * kernels (which may exceed `max`). Not thread-safe against concurrent
+ * recording from several host threads. */
+typedef struct {
+  char name[64];
+  int32_t count;
+  float total_ms;
+} lr_kernel_time;
+
+int lr_profile_enable(int32_t on);
+int lr_profile_collect(lr_kernel_time* out, int32_t max);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* lr_last_error(void);

@@ -343,3 +343,22 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     # the unmodified oracle passes the same check
     with monkeypatch.context() as mp:
         assert _torch_mismatch(mp, (ob, "silu"), ob.silu) < 1e-12
+
+
+def test_primitives_agree_with_block_oracle():
+    """The standalone GEMM definitions reproduce the block's own products."""
+    from oracle import primitives as op
+    s, W, f = small_problem(T=7, d=16, r=4, F=24, seed=14)
+    t = ob.block_forward(W, f["X"], f["O"], s.D, EPS, tape=True)
+    G = ob.block_backward_tape(W, t, f["X"], f["O"], f["dY"], f["dQ"], f["dK"], f["dV"], s.D)
+    Q, K, V = op.grouped_gemm("NT", [(t["q_r"], W["B_q"]), (t["k_r"], W["B_k"]),
+                                     (t["v_r"], W["B_v"])])
+    assert rel_err(Q, t["Q"]) < 1e-14 and rel_err(V, t["V"]) < 1e-14
+    (m,) = op.grouped_gemm("NT", [(t["g_r"], W["B_g"]), (t["u_r"], W["B_u"])], "swiglu")
+    assert rel_err(m, t["m"]) < 1e-14
+    (h,) = op.grouped_gemm("NT", [(t["o_r"], W["B_o"])], "residual", f["X"])
+    assert rel_err(h, t["h"]) < 1e-14
+    (dBdn,) = op.grouped_gemm("TN", [(f["dY"], t["d_r"])])
+    assert rel_err(dBdn, G["B_dn"]) < 1e-14
+    (xn_like,) = op.grouped_gemm("NN", [(f["X"], np.eye(16))], "row_scale", t["rms1"])
+    assert rel_err(W["gamma1"] * xn_like, t["xn"]) < 1e-14
