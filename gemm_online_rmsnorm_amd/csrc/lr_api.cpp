@@ -188,7 +188,39 @@ struct FwdWs {
 struct BwdWs {
   void *h, *dh, *m, *dg, *du, *dd_r, *dgus, *do_r, *dqs;
   float *coef1, *coef2, *colpart;
+  void* wpart;         // split-K partials of the weight gradients
+  size_t wpart_bytes;
 };
+
+// Partial-sum workspace of the largest split-K weight gradient of the block:
+// (M, N, lda, ldb, groups) of every TN GEMM lr_block_bwd runs, K = T.
+size_t wgrad_part_max(const lr_block_shape* s) {
+  const int64_t T = s->T, d = s->d, r = s->r, F = s->d_ff;
+  const int64_t shapes[8][5] = {
+      {d, r, d, r, 1},          // dB_dn
+      {r, F, r, F, 1},          // dA_dn
+      {F, r, F, 2 * r, 2},      // dB_g, dB_u
+      {2 * r, d, 2 * r, d, 1},  // dA_gu
+      {d, r, d, r, 1},          // dB_o
+      {r, d, r, d, 1},          // dA_o
+      {d, r, d, 3 * r, 3},      // dB_q, dB_k, dB_v
+      {3 * r, d, 3 * r, d, 1},  // dA_qkv
+  };
+  size_t mx = 0;
+  for (const auto& sh : shapes) {
+    lr::GemmDesc g;
+    g.M = (int)sh[0];
+    g.N = (int)sh[1];
+    g.K = (int)T;
+    for (int i = 0; i < (int)sh[4]; ++i) {
+      g.lda[i] = sh[2];
+      g.ldb[i] = sh[3];
+    }
+    const size_t b = lr::wgrad_part_bytes(s->dtype, g, (int)sh[4]);
+    mx = b > mx ? b : mx;
+  }
+  return mx;
+}
 
 size_t carve_fwd(const lr_block_shape* s, void* base, FwdWs* out) {
   const size_t e = elem_size(s->dtype);
@@ -217,9 +249,10 @@ size_t carve_bwd(const lr_block_shape* s, void* base, BwdWs* out) {
   w.dqs = c.take(e * s->T * 3 * s->r);
   w.coef1 = static_cast<float*>(c.take(4 * s->T));
   w.coef2 = static_cast<float*>(c.take(4 * s->T));
-  const int bm = lr::gemm_tile_m(lr::OP_NN_RMSBWD, s->dtype);
-  const int64_t tiles = (s->T + bm - 1) / bm;
+  const int64_t tiles = (s->T + lr::kMinTileM - 1) / lr::kMinTileM;
   w.colpart = static_cast<float*>(c.take(4 * tiles * s->d));
+  w.wpart_bytes = wgrad_part_max(s);
+  w.wpart = c.take(w.wpart_bytes);
   if (out) *out = w;
   return c.off + 256;
 }
@@ -239,6 +272,15 @@ int gemm(int op, int dtype, const lr::GemmDesc& d, int groups, hipStream_t st,
          const char* what) {
   ProfScope ps(what, st);
   hipError_t e = lr::run_gemm(op, dtype, d, groups, st);
+  if (e != hipSuccess) return hip_fail(e, what);
+  return LR_OK;
+}
+
+// One weight-gradient GEMM (split-K through the workspace when it pays).
+int wgrad(int dtype, const lr::GemmDesc& d, int groups, const BwdWs& W, hipStream_t st,
+          const char* what) {
+  ProfScope ps(what, st);
+  hipError_t e = lr::run_wgrad(dtype, d, groups, W.wpart, W.wpart_bytes, st);
   if (e != hipSuccess) return hip_fail(e, what);
   return LR_OK;
 }
@@ -559,8 +601,6 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
   const int T = (int)s->T, d = (int)s->d, r = (int)s->r, F = (int)s->d_ff;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float inv_D = 1.0f / (float)s->d_norm;
-  const int bm_rms = lr::gemm_tile_m(lr::OP_NN_RMSBWD, dt);
-  const int tiles_rms = (T + bm_rms - 1) / bm_rms;
 
   if (post) {
     // dB_dn = dY^T d_r
@@ -575,7 +615,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.ldb[0] = r;
       g.c[0] = gr->B_dn;
       g.ldc[0] = r;
-      RUN(gemm(lr::OP_TN_WGRAD, dt, g, 1, st, "dB_dn"));
+      RUN(wgrad(dt, g, 1, W, st, "dB_dn"));
     }
     // dd_r = dY B_dn
     {
@@ -629,7 +669,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.ldb[0] = F;
       g.c[0] = gr->A_dn;
       g.ldc[0] = F;
-      RUN(gemm(lr::OP_TN_WGRAD, dt, g, 1, st, "dA_dn"));
+      RUN(wgrad(dt, g, 1, W, st, "dA_dn"));
     }
     // dB_g = dg^T g_r, dB_u = du^T u_r (grouped)
     {
@@ -649,7 +689,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.ldb[1] = 2 * r;
       g.c[1] = gr->B_u;
       g.ldc[1] = r;
-      RUN(gemm(lr::OP_TN_WGRAD, dt, g, 2, st, "dB_g, dB_u"));
+      RUN(wgrad(dt, g, 2, W, st, "dB_g, dB_u"));
     }
     // dgus = [dg B_g | du B_u] / rms2 (grouped, row-scaled)
     {
@@ -715,8 +755,9 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.rowcoef = W.coef2;
       g.colsum = W.colpart;
       RUN(gemm(lr::OP_NN_RMSBWD, dt, g, 1, st, "RMSNorm-2 backward"));
+      const int bm = lr::gemm_tile_m_used(lr::OP_NN_RMSBWD, dt, g, 1);
       ProfScope ps("dgamma2 column sum", st);
-      hipError_t he = lr::run_colsum(W.colpart, tiles_rms, d, gr->gamma2, st);
+      hipError_t he = lr::run_colsum(W.colpart, (T + bm - 1) / bm, d, gr->gamma2, st);
       if (he != hipSuccess) return hip_fail(he, "dgamma2");
     }
     // dA_gu = gamma2 * (dgus^T h)
@@ -732,7 +773,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.c[0] = gr->A_gu;
       g.ldc[0] = d;
       g.colscale = w->gamma2;
-      RUN(gemm(lr::OP_TN_WGRAD, dt, g, 1, st, "dA_gu"));
+      RUN(wgrad(dt, g, 1, W, st, "dA_gu"));
     }
     // dB_o = dh^T o_r
     {
@@ -746,7 +787,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.ldb[0] = r;
       g.c[0] = gr->B_o;
       g.ldc[0] = r;
-      RUN(gemm(lr::OP_TN_WGRAD, dt, g, 1, st, "dB_o"));
+      RUN(wgrad(dt, g, 1, W, st, "dB_o"));
     }
     // do_r = dh B_o
     {
@@ -774,7 +815,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.ldb[0] = d;
       g.c[0] = gr->A_o;
       g.ldc[0] = d;
-      RUN(gemm(lr::OP_TN_WGRAD, dt, g, 1, st, "dA_o"));
+      RUN(wgrad(dt, g, 1, W, st, "dA_o"));
     }
     // dO = do_r A_o
     {
@@ -810,7 +851,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
         g.c[i] = dBs[i];
         g.ldc[i] = r;
       }
-      RUN(gemm(lr::OP_TN_WGRAD, dt, g, 3, st, "dB_q, dB_k, dB_v"));
+      RUN(wgrad(dt, g, 3, W, st, "dB_q, dB_k, dB_v"));
     }
     // dqs = [dQ B_q | dK B_k | dV B_v] / rms1 (grouped, row-scaled)
     {
@@ -856,8 +897,9 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.rowcoef = W.coef1;
       g.colsum = W.colpart;
       RUN(gemm(lr::OP_NN_RMSBWD, dt, g, 1, st, "RMSNorm-1 backward"));
+      const int bm = lr::gemm_tile_m_used(lr::OP_NN_RMSBWD, dt, g, 1);
       ProfScope ps("dgamma1 column sum", st);
-      hipError_t he = lr::run_colsum(W.colpart, tiles_rms, d, gr->gamma1, st);
+      hipError_t he = lr::run_colsum(W.colpart, (T + bm - 1) / bm, d, gr->gamma1, st);
       if (he != hipSuccess) return hip_fail(he, "dgamma1");
     }
     // dA_qkv = gamma1 * (dqs^T X)
@@ -873,7 +915,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.c[0] = gr->A_qkv;
       g.ldc[0] = d;
       g.colscale = w->gamma1;
-      RUN(gemm(lr::OP_TN_WGRAD, dt, g, 1, st, "dA_qkv"));
+      RUN(wgrad(dt, g, 1, W, st, "dA_qkv"));
     }
   }
   return LR_OK;

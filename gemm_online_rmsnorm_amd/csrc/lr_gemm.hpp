@@ -63,6 +63,12 @@ struct GemmArgs {
   float inv_D;
   float eps;
   int emit_partial;
+  // Split-K (pipelined engine): blockIdx.z = slot + groups * split; split s
+  // covers k-tiles [s * ktiles_split, (s + 1) * ktiles_split) and writes its
+  // output at c[slot] + s * c_split_stride.
+  int groups;
+  int ktiles_split;
+  int64_t c_split_stride;
 };
 
 // ---------------------------------------------------------------------------

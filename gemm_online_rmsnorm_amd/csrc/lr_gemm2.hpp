@@ -1,0 +1,604 @@
+// Pipelined bf16 MFMA GEMM engine for gfx950 (the path for aligned shapes).
+//
+// Operand tiles go from HBM straight into LDS with global_load_lds_dwordx4
+// (16 bytes per lane; a wave's instruction fills one contiguous 1 KB block),
+// through a ring of NSTAGE LDS stages: the loads of K-tile kt + NSTAGE - 1
+// are issued while K-tile kt is multiplied, and one barrier per K-tile
+// separates reuse of a stage. No operand passes through registers on its
+// way to LDS. Both operand storage orders are consumed directly:
+//
+//  * K-contiguous operands ([rows][k]) sit in LDS as rows of BK elements.
+//    The 16-byte chunks of a row are XOR-swizzled so that the 16 lanes of
+//    an MFMA fragment read (16 consecutive rows, one chunk) hit 16 distinct
+//    4-bank groups. Fragments are read with ds_read_b128.
+//  * M/N-contiguous operands ([k][rows]) sit in LDS as k-rows; fragments are
+//    read with ds_read_b64_tr_b16, the transposing LDS read: within a
+//    16-lane group, result lane i element e is element (i & 3) of the
+//    8 bytes addressed by lane 4e + (i >> 2). Pointing lane s at k-row
+//    kb + s/4, columns m0 + 4(s & 3) gives lane i the four values
+//    A[m0 + i][kb .. kb + 3]; two such reads make an MFMA fragment. Chunks
+//    are XOR-swizzled by k-row so the four k-rows of a group and the two
+//    groups read together fall on distinct banks.
+//
+// Requirements (checked by the host): K % BK == 0, 16-byte aligned
+// operands, leading dimensions multiples of 8; M/N-contiguous operands
+// have a row count that is a multiple of 8. Rows beyond M or N are
+// clamped to the last row: they only feed outputs that are never stored.
+//
+// MFMA: v_mfma_f32_16x16x32_bf16. Lane group g = lane / 16 holds
+// k = 8g .. 8g + 7 of each 32-wide k step in both operands; the accumulator
+// of a 16 x 16 tile holds rows 4g + v (v = 0..3) of column lane % 16.
+#pragma once
+
+#include "lr_common.hpp"
+#include "lr_gemm.hpp"
+
+namespace lr {
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+#define LR_GPTR(p) ((__attribute__((address_space(1))) void*)(p))
+#define LR_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int BM_, int BN_, int BK_, int NWM_, int NWN_, int NSTAGE_>
+struct Tile2 {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, NWM = NWM_, NWN = NWN_;
+  static constexpr int NSTAGE = NSTAGE_;
+  static constexpr int NT = 64 * NWM * NWN;
+  static constexpr int NWAVE = NWM * NWN;
+  static constexpr int WTM = BM / NWM, WTN = BN / NWN;
+  static constexpr int FM = WTM / 16, FN = WTN / 16;
+  static constexpr int NSTEP = BK / 32;
+  static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
+};
+
+// Wait until at most N vector-memory operations of this wave are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// ---------------------------------------------------------------------------
+// One operand's DMA loader and fragment reader.
+//   R   rows of the operand tile (BM for A, BN for B)
+//   KC  true: storage [rows][k]; false: storage [k][rows]
+// ---------------------------------------------------------------------------
+template <int R, int BK, int NWAVE, bool KC>
+struct Opnd {
+  static constexpr int BYTES = R * BK * 2;
+  static constexpr int BLOCKS = BYTES / 1024;
+  static_assert(BYTES % 1024 == 0, "tile must be whole 1 KB blocks");
+  static_assert(BLOCKS % NWAVE == 0, "blocks must split over the waves");
+  static constexpr int PER = BLOCKS / NWAVE;  // DMA instructions per lane per stage
+  // KC geometry
+  static constexpr int CPR = BK / 8;          // 16-byte chunks per row
+  static constexpr int RPB = 64 / CPR;        // rows per 1 KB block
+  // MC geometry
+  static constexpr int CPK = R / 8;           // 16-byte chunks per k-row
+  static constexpr int KPB = KC ? 1 : 64 / CPK;
+  static_assert(KC || (R >= 128 && 64 % CPK == 0) || (KC), "M-contiguous tiles need R >= 128");
+
+  int32_t off[PER];  // per-lane element offsets of the loads (tile origin, k0 = 0)
+
+  // Swizzle of a K-contiguous row: flips the chunk index so that 16
+  // consecutive rows at one logical chunk hit 16 distinct bank groups.
+  __device__ static __forceinline__ int swz_kc(int row) {
+    return (BK == 64) ? ((row >> 1) & 7) : ((row >> 2) & 3);
+  }
+  // Swizzle of a k-row of an M-contiguous tile (flips chunk bits 1..3).
+  __device__ static __forceinline__ int swz_mc(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+
+  __device__ __forceinline__ void init(int64_t ld, int r0, int Rtot, int lane, int wave) {
+#pragma unroll
+    for (int v = 0; v < PER; ++v) {
+      const int b = v * NWAVE + wave;
+      if constexpr (KC) {
+        const int row = b * RPB + lane / CPR;
+        const int pc = lane % CPR;
+        const int c = pc ^ swz_kc(row);
+        int gr = r0 + row;
+        gr = gr < Rtot ? gr : Rtot - 1;
+        off[v] = (int32_t)((int64_t)gr * ld + 8 * c);
+      } else {
+        const int k = b * KPB + lane / CPK;
+        const int pc = lane % CPK;
+        const int c = pc ^ swz_mc(k);
+        int gc = r0 / 8 + c;
+        const int last = Rtot / 8 - 1;
+        gc = gc < last ? gc : last;
+        off[v] = (int32_t)((int64_t)k * ld + 8 * gc);
+      }
+    }
+  }
+
+  // Issue this stage's loads: `src` points at the tile's k0 (element (r, k0)
+  // for KC, (k0, r) for MC), `dst` at the stage's LDS tile.
+  __device__ __forceinline__ void issue(const bf16_t* src, unsigned char* dst, int wave) const {
+#pragma unroll
+    for (int v = 0; v < PER; ++v) {
+      const int b = v * NWAVE + wave;
+      __builtin_amdgcn_global_load_lds(LR_GPTR(src + off[v]), LR_LPTR(dst + b * 1024), 16, 0, 0);
+    }
+  }
+
+  // Per-lane byte offsets of fragment reads inside a stage tile, for the
+  // 16-row group starting at row `w0` (a multiple of 16) and k-step `st`.
+  // KC: one ds_read_b128; MC: two ds_read_b64_tr_b16 (4 k-rows apart).
+  __device__ static __forceinline__ int frag_off(int w0, int st, int lane) {
+    const int g = lane >> 4, s = lane & 15;
+    if constexpr (KC) {
+      const int row = w0 + s;
+      const int c = 4 * st + g;
+      return row * (BK * 2) + 16 * (c ^ swz_kc(row));
+    } else {
+      const int k = 32 * st + 8 * g + (s >> 2);
+      const int m = w0 + 4 * (s & 3);
+      return k * (R * 2) + 16 * ((m >> 3) ^ swz_mc(k)) + 2 * (m & 7);
+    }
+  }
+
+  __device__ static __forceinline__ u32x4 read_frag(const unsigned char* tile, int off) {
+    if constexpr (KC) {
+      return *reinterpret_cast<const u32x4*>(tile + off);
+    } else {
+      // The second read is 4 k-rows further down; its swizzle is the same
+      // (k & 3 and (k >> 3) & 1 do not change when k grows by 4 within a
+      // lane's 8-row group).
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4*)(tile + off));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4*)(tile + off + 4 * R * 2));
+      u32x4 r;
+      r[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
+      r[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3));
+      r[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1));
+      r[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3));
+      return r;
+    }
+  }
+};
+
+template <class TL, int NPAIR>
+constexpr int stage_bytes() {
+  return NPAIR * (TL::BM + TL::BN) * TL::BK * 2;
+}
+
+template <class TL>
+constexpr int epi_wave_bytes() {
+  return 16 * (TL::WTN + 4) * 4;
+}
+
+template <class TL, int NPAIR>
+constexpr int gemm2_lds_bytes() {
+  constexpr int ring = TL::NSTAGE * stage_bytes<TL, NPAIR>();
+  constexpr int epi = TL::NWAVE * epi_wave_bytes<TL>() + 2 * TL::BN * 8 * 4;
+  return (ring > epi ? ring : epi) + 8 * TL::BM * 4 /* sums of squares */ + TL::BM * 4;
+}
+
+// ---------------------------------------------------------------------------
+// The kernel.
+// ---------------------------------------------------------------------------
+template <class TL, int NPAIR, uint32_t MCMASK, int EPI>
+__global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
+  constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, S = TL::NSTAGE;
+  constexpr int FM = TL::FM, FN = TL::FN;
+  constexpr bool ORMS = (EPI == EPI_ORMS);
+  constexpr int SB = stage_bytes<TL, NPAIR>();
+  extern __shared__ __align__(16) unsigned char lds[];
+  constexpr int RING = S * SB;
+  constexpr int EPIB = TL::NWAVE * epi_wave_bytes<TL>() + 2 * BN * 8 * 4;
+  constexpr int BODY = RING > EPIB ? RING : EPIB;
+  float* sSS = reinterpret_cast<float*>(lds + BODY);  // [8][BM]
+  float* sRow = sSS + 8 * BM;                          // [BM]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / TL::NWN, wn = wave % TL::NWN;
+  int tm, tn;
+  tile_coords(g.tiles_m, g.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int slot = (NPAIR == 1) ? (int)blockIdx.z % g.groups : 0;
+  const int split = (int)blockIdx.z / g.groups;
+  const int M = g.M, N = g.N;
+
+  using OA0 = Opnd<BM, BK, TL::NWAVE, !(MCMASK & 1u)>;
+  using OB0 = Opnd<BN, BK, TL::NWAVE, !(MCMASK & 2u)>;
+  using OA1 = Opnd<BM, BK, TL::NWAVE, !(MCMASK & 4u)>;
+  using OB1 = Opnd<BN, BK, TL::NWAVE, !(MCMASK & 8u)>;
+  using OA2 = Opnd<BM, BK, TL::NWAVE, !(MCMASK & 16u)>;
+  using OB2 = Opnd<BN, BK, TL::NWAVE, !(MCMASK & 32u)>;
+  OA0 a0;
+  OB0 b0;
+  OA1 a1;
+  OB1 b1;
+  OA2 a2;
+  OB2 b2;
+  const bf16_t* pa[3];
+  const bf16_t* pb[3];
+  int64_t sa[3], sb[3];  // element step of the source pointer per K-tile
+  {
+    const int p0 = slot;
+    pa[0] = static_cast<const bf16_t*>(g.a[p0]);
+    pb[0] = static_cast<const bf16_t*>(g.b[p0]);
+    a0.init(g.lda[p0], m0, M, lane, wave);
+    b0.init(g.ldb[p0], n0, N, lane, wave);
+    sa[0] = (MCMASK & 1u) ? (int64_t)BK * g.lda[p0] : BK;
+    sb[0] = (MCMASK & 2u) ? (int64_t)BK * g.ldb[p0] : BK;
+    if constexpr (NPAIR > 1) {
+      pa[1] = static_cast<const bf16_t*>(g.a[1]);
+      pb[1] = static_cast<const bf16_t*>(g.b[1]);
+      a1.init(g.lda[1], m0, M, lane, wave);
+      b1.init(g.ldb[1], n0, N, lane, wave);
+      sa[1] = (MCMASK & 4u) ? (int64_t)BK * g.lda[1] : BK;
+      sb[1] = (MCMASK & 8u) ? (int64_t)BK * g.ldb[1] : BK;
+    }
+    if constexpr (NPAIR > 2) {
+      pa[2] = static_cast<const bf16_t*>(g.a[2]);
+      pb[2] = static_cast<const bf16_t*>(g.b[2]);
+      a2.init(g.lda[2], m0, M, lane, wave);
+      b2.init(g.ldb[2], n0, N, lane, wave);
+      sa[2] = (MCMASK & 16u) ? (int64_t)BK * g.lda[2] : BK;
+      sb[2] = (MCMASK & 32u) ? (int64_t)BK * g.ldb[2] : BK;
+    }
+    // The per-lane offsets hold the (clamped) rows / chunks relative to the
+    // matrix start; a split starts its sources at its first k-tile.
+    const int64_t kt0 = (int64_t)split * g.ktiles_split;
+#pragma unroll
+    for (int p = 0; p < NPAIR; ++p) {
+      pa[p] += kt0 * sa[p];
+      pb[p] += kt0 * sb[p];
+    }
+  }
+  auto stage_ptr = [&](int s) { return lds + s * SB; };
+  auto issue = [&](int kt) {
+    unsigned char* st = stage_ptr(kt % S);
+    a0.issue(pa[0] + kt * sa[0], st, wave);
+    b0.issue(pb[0] + kt * sb[0], st + BM * BK * 2, wave);
+    if constexpr (NPAIR > 1) {
+      a1.issue(pa[1] + kt * sa[1], st + (BM + BN) * BK * 2, wave);
+      b1.issue(pb[1] + kt * sb[1], st + (2 * BM + BN) * BK * 2, wave);
+    }
+    if constexpr (NPAIR > 2) {
+      a2.issue(pa[2] + kt * sa[2], st + 2 * (BM + BN) * BK * 2, wave);
+      b2.issue(pb[2] + kt * sb[2], st + (3 * BM + 2 * BN) * BK * 2, wave);
+    }
+  };
+  constexpr int L = OA0::PER + OB0::PER + (NPAIR > 1 ? OA1::PER + OB1::PER : 0) +
+                    (NPAIR > 2 ? OA2::PER + OB2::PER : 0);
+  static_assert(L * (S - 1) < 64, "too many loads in flight for vmcnt");
+
+  f32x4 acc[NPAIR][FM][FN];
+#pragma unroll
+  for (int p = 0; p < NPAIR; ++p)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[p][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Per-lane fragment offsets (k-step 0; step 1 adds a constant).
+  const int w0m = wm * TL::WTM, w0n = wn * TL::WTN;
+
+  float ssp[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) ssp[i] = 0.f;
+  int panel = 0, in_panel = 0;
+
+  const int nk = g.ktiles_split;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // Stage kt is complete when at most (stages issued after it) x L loads
+    // of this lane remain.
+    const int after = min(nk - 1 - kt, S - 2);
+    if constexpr (S >= 4) {
+      if (after >= 2) wait_vmcnt<2 * L>();
+      else if (after == 1) wait_vmcnt<L>();
+      else wait_vmcnt<0>();
+    } else if constexpr (S == 3) {
+      if (after >= 1) wait_vmcnt<L>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    block_barrier();
+    if (kt + S - 1 < nk) issue(kt + S - 1);
+
+    const unsigned char* st = stage_ptr(kt % S);
+#pragma unroll
+    for (int p = 0; p < NPAIR; ++p) {
+      const unsigned char* tA = st + p * (BM + BN) * BK * 2;
+      const unsigned char* tB = tA + BM * BK * 2;
+#pragma unroll
+      for (int s = 0; s < TL::NSTEP; ++s) {
+        u32x4 af[FM], bfr[FN];
+        const bool amc = (MCMASK >> (2 * p)) & 1u;
+        const bool bmc = (MCMASK >> (2 * p + 1)) & 1u;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          if (amc)
+            af[i] = Opnd<BM, BK, TL::NWAVE, false>::read_frag(
+                tA, Opnd<BM, BK, TL::NWAVE, false>::frag_off(w0m + 16 * i, s, lane));
+          else
+            af[i] = Opnd<BM, BK, TL::NWAVE, true>::read_frag(
+                tA, Opnd<BM, BK, TL::NWAVE, true>::frag_off(w0m + 16 * i, s, lane));
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if (bmc)
+            bfr[j] = Opnd<BN, BK, TL::NWAVE, false>::read_frag(
+                tB, Opnd<BN, BK, TL::NWAVE, false>::frag_off(w0n + 16 * j, s, lane));
+          else
+            bfr[j] = Opnd<BN, BK, TL::NWAVE, true>::read_frag(
+                tB, Opnd<BN, BK, TL::NWAVE, true>::frag_off(w0n + 16 * j, s, lane));
+        }
+        if constexpr (ORMS) {
+          if (p == 0 && wn == 0) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float lo = bf16_lo(af[i][q]), hi = bf16_hi(af[i][q]);
+                ssp[i] = __builtin_fmaf(lo, lo, ssp[i]);
+                ssp[i] = __builtin_fmaf(hi, hi, ssp[i]);
+              }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) mfma_step<bf16_t>(af[i], bfr[j], acc[p][i][j]);
+      }
+    }
+    if constexpr (ORMS) {
+      if (++in_panel == g.panel_ktiles || kt == nk - 1) {
+        if (wn == 0) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            float x = ssp[i];
+            x += __shfl_xor(x, 16, 64);
+            x += __shfl_xor(x, 32, 64);
+            if (lane < 16) sSS[panel * BM + w0m + 16 * i + lane] = x;
+            ssp[i] = 0.f;
+          }
+        }
+        ++panel;
+        in_panel = 0;
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with the ring; sSS is visible
+
+  if constexpr (ORMS) {
+    for (int r = tid; r < BM; r += TL::NT) {
+      float ss = 0.f;
+      for (int p = 0; p < g.n_panels; ++p) ss += sSS[p * BM + r];
+      const float rmsg = sqrtf(ss * g.inv_D + g.eps);
+      sRow[r] = g.emit_partial ? 1.0f : 1.0f / rmsg;
+      const int gr = m0 + r;
+      if (tn == 0 && gr < M) {
+        if (g.rms_out && !g.emit_partial) g.rms_out[gr] = rmsg;
+        if (g.ss_out) {
+          if (g.emit_partial) {
+            g.ss_out[gr] = ss;
+          } else {
+            for (int p = 0; p < g.n_panels; ++p) g.ss_out[(int64_t)p * M + gr] = sSS[p * BM + r];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // Elementwise combination of the accumulators.
+  if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float gg = acc[0][i][j][v];
+          acc[0][i][j][v] = gg * sigmoid_f<bf16_t>(gg) * acc[1][i][j][v];
+        }
+  }
+  if constexpr (EPI == EPI_SWIGLU_BWD) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float gg = acc[0][i][j][v], uu = acc[1][i][j][v], dm = acc[2][i][j][v];
+          const float sg = sigmoid_f<bf16_t>(gg);
+          const float sl = gg * sg;
+          acc[0][i][j][v] = sl * uu;
+          acc[1][i][j][v] = dm * uu * sg * (1.0f + gg * (1.0f - sg));
+          acc[2][i][j][v] = dm * sl;
+        }
+  }
+
+  // Wave-private staging: one 16-row band of the wave tile at a time. Each
+  // lane owns PERL chunks of 8 columns per band, always at the same column
+  // offset, so per-column inputs (gamma) are loaded once; the per-row and
+  // per-element inputs of band i + 1 are loaded while band i is written.
+  constexpr int CPW = TL::WTN + 4;
+  float* sW = reinterpret_cast<float*>(lds + wave * epi_wave_bytes<TL>());
+  constexpr int CH = TL::WTN / 8;           // 8-column chunks per band row
+  constexpr int PERL = 16 * CH / 64;        // chunks per lane per band
+  static_assert((16 * CH) % 64 == 0, "band must split over the lanes");
+  static_assert(64 % CH == 0, "a lane's column chunk must not change across its band chunks");
+  constexpr int NOUT = (EPI == EPI_SWIGLU_BWD) ? 3 : 1;
+  constexpr bool HAS_RES = (EPI == EPI_STORE || EPI == EPI_RMSBWD);
+  constexpr bool HAS_H = (EPI == EPI_RMSBWD);
+  constexpr bool HAS_GAMMA = (EPI == EPI_RMSBWD || EPI == EPI_WGRAD);
+  constexpr bool HAS_ROW = (EPI == EPI_STORE || EPI == EPI_RMSBWD);
+  const int c8l = (lane % CH) * 8;             // this lane's column chunk in the band
+  const int gcl = n0 + w0n + c8l;              // its global column
+  const int nvl = N - gcl;                     // valid columns of the chunk
+  const bool col_ok = gcl < N;
+  float colacc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) colacc[e] = 0.f;
+  float gm[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gm[e] = 1.0f;
+  if constexpr (HAS_GAMMA) {
+    if (g.colscale && col_ok) gload8<bf16_t>(static_cast<const bf16_t*>(g.colscale) + gcl, nvl, gm);
+  }
+  const bf16_t* resp = static_cast<const bf16_t*>(g.res);
+  const bf16_t* hp = static_cast<const bf16_t*>(g.hsrc);
+  const float* rowp = (EPI == EPI_RMSBWD) ? g.rowcoef : g.rowdiv;
+
+  // Raw per-band inputs of one lane: PERL chunks of residual / H and a row scalar.
+  struct BandIn {
+    u32x4 r[PERL], h[PERL];
+    float f[PERL];
+  };
+  auto load_band = [&](int i, BandIn& in) {
+#pragma unroll
+    for (int q = 0; q < PERL; ++q) {
+      const int rr = (lane + 64 * q) / CH;
+      const int gr = m0 + w0m + 16 * i + rr;
+      const bool ok = col_ok && gr < M;
+      in.r[q] = u32x4{0u, 0u, 0u, 0u};
+      in.h[q] = u32x4{0u, 0u, 0u, 0u};
+      in.f[q] = 1.0f;
+      if constexpr (HAS_RES) {
+        if (ok && resp) {
+          const bf16_t* src = resp + (int64_t)gr * g.ldres + gcl;
+          if (nvl >= 8) {
+            in.r[q] = *reinterpret_cast<const u32x4*>(src);
+          } else {
+            float t[8];
+            gload8<bf16_t>(src, nvl, t);
+            in.r[q] = pack16<bf16_t>(t);
+          }
+        }
+      }
+      if constexpr (HAS_H) {
+        if (ok) {
+          const bf16_t* src = hp + (int64_t)gr * g.ldh + gcl;
+          if (nvl >= 8) {
+            in.h[q] = *reinterpret_cast<const u32x4*>(src);
+          } else {
+            float t[8];
+            gload8<bf16_t>(src, nvl, t);
+            in.h[q] = pack16<bf16_t>(t);
+          }
+        }
+      }
+      if constexpr (HAS_ROW) {
+        if (ok && rowp) in.f[q] = rowp[gr];
+      }
+    }
+  };
+
+#pragma unroll
+  for (int o = 0; o < NOUT; ++o) {
+    const int ao = (EPI == EPI_SWIGLU_BWD) ? o : 0;
+    BandIn cur, nxt;
+    if constexpr (HAS_RES || HAS_ROW) load_band(0, cur);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if constexpr (HAS_RES || HAS_ROW) {
+        if (i + 1 < FM) load_band(i + 1, nxt);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          sW[(4 * (lane >> 4) + v) * CPW + 16 * j + (lane & 15)] = acc[ao][i][j][v];
+#pragma unroll
+      for (int q = 0; q < PERL; ++q) {
+        const int id = lane + 64 * q;
+        const int rr = id / CH;
+        const int lrow = w0m + 16 * i + rr;  // row within the block tile
+        const int gr = m0 + lrow;
+        float v[8];
+        {
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(sW + rr * CPW + c8l);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(sW + rr * CPW + c8l + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = x0[e];
+            v[4 + e] = x1[e];
+          }
+        }
+        if (gr >= M || !col_ok) continue;
+        if constexpr (EPI == EPI_STORE) {
+          if (rowp) {
+            const float sc = 1.0f / cur.f[q];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] *= sc;
+          }
+          if (resp) {
+            float rv[8];
+            unpack16<bf16_t>(cur.r[q], rv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += rv[e];
+          }
+          gstore8<bf16_t>(static_cast<bf16_t*>(g.c[slot]) + (int64_t)gr * g.ldc[slot] + gcl, nvl, v);
+        } else if constexpr (EPI == EPI_ORMS) {
+          const float sc = sRow[lrow];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= sc;
+          gstore8<bf16_t>(static_cast<bf16_t*>(g.c[0]) + (int64_t)gr * g.ldc[0] + gcl, nvl, v);
+        } else if constexpr (EPI == EPI_SWIGLU) {
+          gstore8<bf16_t>(static_cast<bf16_t*>(g.c[0]) + (int64_t)gr * g.ldc[0] + gcl, nvl, v);
+        } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+          gstore8<bf16_t>(static_cast<bf16_t*>(g.c[o]) + (int64_t)gr * g.ldc[o] + gcl, nvl, v);
+        } else if constexpr (EPI == EPI_RMSBWD) {
+          float hv[8], rv[8];
+          unpack16<bf16_t>(cur.h[q], hv);
+          unpack16<bf16_t>(cur.r[q], rv);
+          const float cf = cur.f[q];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            colacc[e] += v[e] * hv[e];
+            v[e] = rv[e] + gm[e] * v[e] - cf * hv[e];
+          }
+          gstore8<bf16_t>(static_cast<bf16_t*>(g.c[0]) + (int64_t)gr * g.ldc[0] + gcl, nvl, v);
+        } else if constexpr (EPI == EPI_WGRAD) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= gm[e];
+          gstore8<float>(static_cast<float*>(g.c[slot]) + split * g.c_split_stride +
+                             (int64_t)gr * g.ldc[slot] + gcl, nvl, v);
+        }
+      }
+      if constexpr (HAS_RES || HAS_ROW) {
+        if (i + 1 < FM) cur = nxt;
+      }
+    }
+  }
+
+  if constexpr (EPI == EPI_RMSBWD) {
+    // Column sums of acc * H over this tile's rows, in a fixed order:
+    // lanes sharing columns (lane % CH) first, then the NWM waves of a column
+    // band through LDS.
+    static_assert(64 % CH == 0, "lanes must tile the band's chunks");
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+      for (int off = CH; off < 64; off <<= 1) colacc[e] += __shfl_xor(colacc[e], off, 64);
+    }
+    float* sCol = reinterpret_cast<float*>(lds + TL::NWAVE * epi_wave_bytes<TL>());  // [NWM][BN]
+    if (lane < CH) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sCol[wm * BN + w0n + lane * 8 + e] = colacc[e];
+    }
+    __syncthreads();
+    for (int c = tid; c < BN; c += TL::NT) {
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < TL::NWM; ++q) s += sCol[q * BN + c];
+      if (n0 + c < N) g.colsum[(int64_t)tm * N + n0 + c] = s;
+    }
+  }
+}
+
+}  // namespace lr

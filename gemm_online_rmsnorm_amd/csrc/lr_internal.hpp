@@ -43,6 +43,8 @@ struct GemmDesc {
   float inv_D = 0.f;
   float eps = 0.f;
   int emit_partial = 0;
+  int ksplit = 1;                // split-K factor (pipelined engine only)
+  int64_t c_split_stride = 0;    // output element stride between splits
 };
 
 // Tile sizes an operation uses for a dtype (0 = LR_F32, 1 = LR_BF16).
@@ -51,6 +53,25 @@ int gemm_tile_k(int op, int dtype);
 
 // Enqueue one GEMM launch over `groups` operand groups (grid z).
 hipError_t run_gemm(int op, int dtype, const GemmDesc& d, int groups, hipStream_t s);
+
+// Whether run_gemm takes the pipelined engine for this call, and the M-tile
+// it then uses (the RMSNorm-backward column partials have one row per M-tile).
+bool uses_engine2(int op, int dtype, const GemmDesc& d, int groups);
+int gemm2_tile_m(int op, const GemmDesc& d, int groups);
+void set_engine2(bool on);
+// M-tile of the kernel run_gemm dispatches for this call.
+int gemm_tile_m_used(int op, int dtype, const GemmDesc& d, int groups);
+// Smallest M-tile any GEMM kernel uses (sizes per-M-tile workspaces).
+constexpr int kMinTileM = 64;
+
+// Weight-gradient (TN) GEMM with deterministic split-K: when the output grid
+// is too small to fill the chip, K is cut into slices whose fp32 partials go
+// to `part` (part_bytes long) and are then added in a fixed order, with the
+// column scale applied, into d.c[slot]. Without split the GEMM writes d.c
+// directly. wgrad_part_bytes gives the partial workspace a call needs.
+size_t wgrad_part_bytes(int dtype, const GemmDesc& d, int groups);
+hipError_t run_wgrad(int dtype, const GemmDesc& d, int groups, void* part, size_t part_bytes,
+                     hipStream_t s);
 
 // Memory-bound helpers.
 hipError_t run_fold_gamma(int dtype, const void* A, int64_t lda, const void* gamma, void* out,

@@ -1,10 +1,12 @@
 // Kernels of the low-rank block for gfx950: GEMM instantiations and the
 // memory-bound helpers (gamma folding, r-wide row dots, column reductions,
 // rank-share finalisation).
+#include <algorithm>
 #include <mutex>
 
 #include "lr_common.hpp"
 #include "lr_gemm.hpp"
+#include "lr_gemm2.hpp"
 #include "lr_internal.hpp"
 
 namespace lr {
@@ -72,6 +74,9 @@ static hipError_t launch(const GemmDesc& d, int groups, hipStream_t s) {
   g.inv_D = d.inv_D;
   g.eps = d.eps;
   g.emit_partial = d.emit_partial;
+  g.groups = groups;
+  g.ktiles_split = ktiles_total;
+  g.c_split_stride = 0;
   if (g.tiles_m == 0 || g.tiles_n == 0 || groups == 0) return hipSuccess;
   dim3 grid(g.tiles_m * g.tiles_n, 1, groups);
   hipLaunchKernelGGL(kern, grid, dim3(TL::NT), lds, s, g);
@@ -100,7 +105,257 @@ static hipError_t dispatch(int op, const GemmDesc& d, int groups, hipStream_t s)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined engine (lr_gemm2.hpp) for bf16 GEMMs with K a multiple of the
+// k-tile. The large tile is 256 x 256 with 8 waves (two per SIMD, 128 x 64
+// each), so that one wave's barrier and LDS waits are covered by the other
+// wave's MFMAs; smaller grids fall back to 256 x 128 or 128 x 128 tiles with
+// 4 waves. The two- and three-pair GEMMs use k-tiles of 32 in three stages.
+// ---------------------------------------------------------------------------
+using P256x256 = Tile2<256, 256, 64, 2, 4, 2>;
+using P256x128 = Tile2<256, 128, 64, 2, 2, 2>;
+using P128x128 = Tile2<128, 128, 64, 2, 2, 2>;
+using P2x256x128 = Tile2<256, 128, 32, 4, 2, 3>;
+using P2x128x128 = Tile2<128, 128, 32, 2, 2, 3>;
+using P3x128x128 = Tile2<128, 128, 32, 2, 4, 3>;
+
+template <class TL, int NPAIR, uint32_t MC, int EPI>
+static hipError_t launch2(const GemmDesc& d, int groups, hipStream_t s) {
+  auto kern = gemm2_kernel<TL, NPAIR, MC, EPI>;
+  constexpr int lds = gemm2_lds_bytes<TL, NPAIR>();
+  static_assert(lds <= 160 * 1024, "LDS budget exceeded");
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [&] {
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  GemmArgs g{};
+  g.M = d.M;
+  g.N = d.N;
+  g.K = d.K;
+  g.tiles_m = (d.M + TL::BM - 1) / TL::BM;
+  g.tiles_n = (d.N + TL::BN - 1) / TL::BN;
+  for (int i = 0; i < 3; ++i) {
+    g.a[i] = d.a[i];
+    g.lda[i] = d.lda[i];
+    g.b[i] = d.b[i];
+    g.ldb[i] = d.ldb[i];
+    g.c[i] = d.c[i];
+    g.ldc[i] = d.ldc[i];
+  }
+  g.res = d.res;
+  g.ldres = d.ldres;
+  g.hsrc = d.hsrc;
+  g.ldh = d.ldh;
+  g.rowdiv = d.rowdiv;
+  g.rowcoef = d.rowcoef;
+  g.colscale = d.colscale;
+  g.colsum = d.colsum;
+  g.rms_out = d.rms_out;
+  g.ss_out = d.ss_out;
+  g.n_panels = d.n_panels;
+  g.panel_ktiles = (d.n_panels > 1) ? d.panel_width / TL::BK : d.K / TL::BK;
+  g.inv_D = d.inv_D;
+  g.eps = d.eps;
+  g.emit_partial = d.emit_partial;
+  g.groups = groups;
+  const int split = d.ksplit > 1 ? d.ksplit : 1;
+  g.ktiles_split = d.K / TL::BK / split;
+  g.c_split_stride = d.c_split_stride;
+  if (g.tiles_m == 0 || g.tiles_n == 0 || groups == 0) return hipSuccess;
+  dim3 grid(g.tiles_m * g.tiles_n, 1, groups * split);
+  hipLaunchKernelGGL(kern, grid, dim3(TL::NT), lds, s, g);
+  return hipGetLastError();
+}
+
+static int64_t ntiles(const GemmDesc& d, int bm, int bn, int groups) {
+  return (int64_t)((d.M + bm - 1) / bm) * ((d.N + bn - 1) / bn) * groups;
+}
+
+// Whether the pipelined engine can run this GEMM: k-tiles divide K, the
+// M/N-contiguous operands have whole 8-element chunks, every per-lane load
+// offset fits in 32 bits, and the Online RMSNorm panels are whole k-tiles.
+static bool eligible2(int op, const GemmDesc& d, int groups, int bk) {
+  if (d.K % bk != 0 || d.M < 1 || d.N < 1) return false;
+  uint32_t mc = 0;
+  int npair = 1;
+  switch (op) {
+    case OP_NN_STORE:
+    case OP_NN_RMSBWD: mc = 2u; break;
+    case OP_TN_WGRAD: mc = 3u; break;
+    case OP_SWIGLU_BWD: mc = 32u; npair = 3; break;
+    case OP_NT_SWIGLU: npair = 2; break;
+    default: break;
+  }
+  const int nsl = (npair == 1) ? groups : npair;
+  for (int p = 0; p < nsl; ++p) {
+    const int lp = (npair == 1) ? 0 : p;  // the groups of a grouped GEMM share pair 0's layout
+    const bool amc = (mc >> (2 * lp)) & 1u, bmc = (mc >> (2 * lp + 1)) & 1u;
+    if (amc ? (d.M % 8 != 0) : ((int64_t)d.M * d.lda[p] >= ((int64_t)1 << 31))) return false;
+    if (bmc ? (d.N % 8 != 0) : ((int64_t)d.N * d.ldb[p] >= ((int64_t)1 << 31))) return false;
+    if (amc && (int64_t)bk * d.lda[p] >= ((int64_t)1 << 31)) return false;
+    if (bmc && (int64_t)bk * d.ldb[p] >= ((int64_t)1 << 31)) return false;
+  }
+  if (op == OP_NT_ORMS && d.n_panels > 1 && d.panel_width % bk != 0) return false;
+  return true;
+}
+
+static constexpr int kCUs = 256;
+
+// Fraction of the CU slots the last partial wave of workgroups leaves busy.
+static double wave_eff(int64_t tiles) {
+  const int64_t waves = (tiles + kCUs - 1) / kCUs;
+  return waves ? (double)tiles / (double)(waves * kCUs) : 0.0;
+}
+
+// Tile choice of the single-pair GEMMs: the 256 x 256 tile unless its grid
+// leaves most CUs idle, then 256 x 128, then 128 x 128.
+static int single_tile(const GemmDesc& d, int groups) {
+  const int64_t t256 = ntiles(d, 256, 256, groups), t128 = ntiles(d, 256, 128, groups);
+  if (t256 >= kCUs && wave_eff(t256) >= 0.75) return 0;
+  if (t128 >= kCUs && wave_eff(t128) >= 0.75) return 1;
+  if (t256 >= kCUs) return 0;
+  if (t128 >= kCUs) return 1;
+  return 2;
+}
+
+template <int EPI, uint32_t MC>
+static hipError_t launch_single(const GemmDesc& d, int groups, hipStream_t s) {
+  switch (single_tile(d, groups)) {
+    case 0: return launch2<P256x256, 1, MC, EPI>(d, groups, s);
+    case 1: return launch2<P256x128, 1, MC, EPI>(d, groups, s);
+    default: return launch2<P128x128, 1, MC, EPI>(d, groups, s);
+  }
+}
+
+// Weight gradients: 256 x 256 tiles when both output sides allow it, and a
+// split of K that minimises (waves of workgroups) / (split) plus a small cost
+// per extra split for the partial-sum traffic.
+static bool wgrad_big_tile(const GemmDesc& d) { return d.M >= 256 && d.N >= 256; }
+
+static int wgrad_split(const GemmDesc& d, int groups) {
+  const bool big = wgrad_big_tile(d);
+  const int64_t t = ntiles(d, big ? 256 : 128, big ? 256 : 128, groups);
+  const int nk = d.K / 64;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int sp : {1, 2, 3, 4, 6, 8}) {
+    if (nk % sp != 0 || nk / sp < 4) continue;
+    const double waves = (double)((t * sp + kCUs - 1) / kCUs);
+    const double cost = waves / sp + 0.03 * (sp - 1);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = sp;
+    }
+  }
+  return best;
+}
+
+static hipError_t run_gemm2(int op, const GemmDesc& d, int groups, hipStream_t s) {
+  if (op == OP_TN_WGRAD) {
+    if (wgrad_big_tile(d)) return launch2<P256x256, 1, 3u, EPI_WGRAD>(d, groups, s);
+    return launch2<P128x128, 1, 3u, EPI_WGRAD>(d, groups, s);
+  }
+  switch (op) {
+    case OP_NT_STORE: return launch_single<EPI_STORE, 0u>(d, groups, s);
+    case OP_NT_ORMS: return launch_single<EPI_ORMS, 0u>(d, groups, s);
+    case OP_NN_STORE: return launch_single<EPI_STORE, 2u>(d, groups, s);
+    case OP_NN_RMSBWD: return launch_single<EPI_RMSBWD, 2u>(d, groups, s);
+    case OP_NT_SWIGLU:
+      if (ntiles(d, 256, 128, 1) >= kCUs) return launch2<P2x256x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
+      return launch2<P2x128x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
+    case OP_SWIGLU_BWD: return launch2<P3x128x128, 3, 32u, EPI_SWIGLU_BWD>(d, 1, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+static int engine2_bk(int op) {
+  return (op == OP_NT_SWIGLU || op == OP_SWIGLU_BWD) ? 32 : 64;
+}
+
+static bool g_engine2 = true;
+
+void set_engine2(bool on) { g_engine2 = on; }
+
+int gemm2_tile_m(int op, const GemmDesc& d, int groups) {
+  if (op == OP_NT_SWIGLU) return ntiles(d, 256, 128, 1) >= kCUs ? 256 : 128;
+  if (op == OP_SWIGLU_BWD) return 128;
+  return single_tile(d, groups) == 2 ? 128 : 256;
+}
+
+bool uses_engine2(int op, int dtype, const GemmDesc& d, int groups) {
+  return g_engine2 && dtype == 1 && eligible2(op, d, groups, engine2_bk(op));
+}
+
+int gemm_tile_m_used(int op, int dtype, const GemmDesc& d, int groups) {
+  return uses_engine2(op, dtype, d, groups) ? gemm2_tile_m(op, d, groups)
+                                            : gemm_tile_m(op, dtype);
+}
+
+// out[slot][i, j] = colscale[j] * sum_s part[s][slot][i, j], s in order.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            int splits, int64_t split_stride,
+                                                            int64_t count, int n,
+                                                            const bf16_t* __restrict__ colscale,
+                                                            float* __restrict__ out, int64_t ldo) {
+  const int64_t nq = count / 4;
+  for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < nq;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = q * 4;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(part + e);
+    for (int sp = 1; sp < splits; ++sp)
+      acc += *reinterpret_cast<const f32x4*>(part + sp * split_stride + e);
+    const int64_t row = e / n;
+    const int col = (int)(e % n);
+    if (colscale) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] *= Elem<bf16_t>::load(colscale + col + k);
+    }
+    *reinterpret_cast<f32x4*>(out + row * ldo + col) = acc;
+  }
+}
+
+size_t wgrad_part_bytes(int dtype, const GemmDesc& d, int groups) {
+  if (!uses_engine2(OP_TN_WGRAD, dtype, d, groups)) return 0;
+  const int sp = wgrad_split(d, groups);
+  if (sp <= 1) return 0;
+  return (size_t)sp * groups * (size_t)d.M * d.N * sizeof(float);
+}
+
+hipError_t run_wgrad(int dtype, const GemmDesc& d, int groups, void* part, size_t part_bytes,
+                     hipStream_t s) {
+  const size_t need = wgrad_part_bytes(dtype, d, groups);
+  if (need == 0 || part == nullptr || part_bytes < need || d.N % 4 != 0)
+    return run_gemm(OP_TN_WGRAD, dtype, d, groups, s);
+  GemmDesc q = d;
+  q.ksplit = wgrad_split(d, groups);
+  const int64_t mn = (int64_t)d.M * d.N;
+  q.c_split_stride = groups * mn;
+  q.colscale = nullptr;
+  float* pbase = static_cast<float*>(part);
+  for (int gidx = 0; gidx < groups; ++gidx) {
+    q.c[gidx] = pbase + gidx * mn;
+    q.ldc[gidx] = d.N;
+  }
+  hipError_t e = run_gemm2(OP_TN_WGRAD, q, groups, s);
+  if (e != hipSuccess) return e;
+  for (int gidx = 0; gidx < groups; ++gidx) {
+    const int64_t nq = mn / 4;
+    int grid = (int)std::min<int64_t>((nq + 255) / 256, 8192);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, s, pbase + gidx * mn,
+                       q.ksplit, q.c_split_stride, mn, d.N,
+                       static_cast<const bf16_t*>(d.colscale), static_cast<float*>(d.c[gidx]),
+                       d.ldc[gidx]);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t run_gemm(int op, int dtype, const GemmDesc& d, int groups, hipStream_t s) {
+  if (uses_engine2(op, dtype, d, groups)) return run_gemm2(op, d, groups, s);
   if (dtype == 0) return dispatch<float, TF32, TF32, TF32>(op, d, groups, s);
   return dispatch<bf16_t, TBig, TMid, TMid>(op, d, groups, s);
 }
@@ -158,14 +413,19 @@ __global__ __launch_bounds__(256) void rowdot_coef_kernel(const T* __restrict__ 
   }
 }
 
-// out[c] = sum_t part[t, c], t in a fixed order.
+// out[c] = sum_t part[t, c] in a fixed order: four row groups of a block
+// each add every fourth partial row, then the four sums are added in order.
 __global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ part, int tiles,
                                                      int n, float* __restrict__ out) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= n) return;
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
   float s = 0.f;
-  for (int t = 0; t < tiles; ++t) s += part[(int64_t)t * n + c];
-  out[c] = s;
+  if (c < n)
+    for (int t = q; t < tiles; t += 4) s += part[(int64_t)t * n + c];
+  red[q][lane] = s;
+  __syncthreads();
+  if (q == 0 && c < n) out[c] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
 }
 
 // Rank-share finalisation after the (identity) all-reduce:
@@ -233,7 +493,7 @@ hipError_t run_rowdot_coef(int dtype, const void* a, int64_t lda, const void* b,
 }
 
 hipError_t run_colsum(const float* part, int tiles, int n, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(colsum_kernel, dim3((n + 255) / 256), dim3(256), 0, s, part, tiles, n, out);
+  hipLaunchKernelGGL(colsum_kernel, dim3((n + 63) / 64), dim3(256), 0, s, part, tiles, n, out);
   return hipGetLastError();
 }
 
