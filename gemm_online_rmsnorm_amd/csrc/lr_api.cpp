@@ -655,7 +655,31 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.ldc[1] = F;
       g.c[2] = W.du;
       g.ldc[2] = F;
-      RUN(gemm(lr::OP_SWIGLU_BWD, dt, g, 1, st, "SwiGLU recompute + backward"));
+      // On the pipelined engine dm = dd_r A_dn is its own GEMM (written into
+      // du's buffer), then one two-pair tile recomputes g and u and reads dm
+      // in its epilogue, which overwrites dm with du element by element.
+      lr::GemmDesc dmg;
+      dmg.M = T;
+      dmg.N = F;
+      dmg.K = r;
+      dmg.a[0] = W.dd_r;
+      dmg.lda[0] = r;
+      dmg.b[0] = w->A_dn;
+      dmg.ldb[0] = F;
+      dmg.c[0] = W.du;
+      dmg.ldc[0] = F;
+      lr::GemmDesc two = g;
+      two.a[2] = nullptr;
+      two.b[2] = nullptr;
+      two.res = W.du;
+      two.ldres = F;
+      if (lr::uses_engine2(lr::OP_NN_STORE, dt, dmg, 1) &&
+          lr::uses_engine2(lr::OP_SWIGLU_BWD2, dt, two, 1)) {
+        RUN(gemm(lr::OP_NN_STORE, dt, dmg, 1, st, "dm = dd_r A_dn"));
+        RUN(gemm(lr::OP_SWIGLU_BWD2, dt, two, 1, st, "SwiGLU recompute + backward"));
+      } else {
+        RUN(gemm(lr::OP_SWIGLU_BWD, dt, g, 1, st, "SwiGLU recompute + backward"));
+      }
     }
     // dA_dn = dd_r^T m
     {

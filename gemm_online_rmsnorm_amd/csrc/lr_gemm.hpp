@@ -34,6 +34,7 @@ enum EpiKind : int {
   EPI_SWIGLU_BWD = 3,  // acc0 = g, acc1 = u, acc2 = dm -> m, dg, du
   EPI_RMSBWD = 4,      // out = res + gamma[col]*acc - coef[row]*H; colsum(acc*H)
   EPI_WGRAD = 5,       // fp32 out = acc [* colscale[col]]
+  EPI_SWIGLU_BWD2 = 6, // acc0 = g, acc1 = u, res = dm -> m, dg, du (pipelined engine)
 };
 
 struct GemmArgs {

@@ -433,7 +433,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   static_assert((16 * CH) % 64 == 0, "band must split over the lanes");
   static_assert(64 % CH == 0, "a lane's column chunk must not change across its band chunks");
   constexpr int NOUT = (EPI == EPI_SWIGLU_BWD) ? 3 : 1;
-  constexpr bool HAS_RES = (EPI == EPI_STORE || EPI == EPI_RMSBWD);
+  constexpr bool HAS_RES = (EPI == EPI_STORE || EPI == EPI_RMSBWD || EPI == EPI_SWIGLU_BWD2);
   constexpr bool HAS_H = (EPI == EPI_RMSBWD);
   constexpr bool HAS_GAMMA = (EPI == EPI_RMSBWD || EPI == EPI_WGRAD);
   constexpr bool HAS_ROW = (EPI == EPI_STORE || EPI == EPI_RMSBWD);
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       in.h[q] = u32x4{0u, 0u, 0u, 0u};
       in.f[q] = 1.0f;
       if constexpr (HAS_RES) {
-        if (ok && resp) {
+        if (ok && resp) {  // residual, upstream gradient or dm
           const bf16_t* src = resp + (int64_t)gr * g.ldres + gcl;
           if (nvl >= 8) {
             in.r[q] = *reinterpret_cast<const u32x4*>(src);
@@ -513,6 +513,48 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           sW[(4 * (lane >> 4) + v) * CPW + 16 * j + (lane & 15)] = acc[ao][i][j][v];
+      // SwiGLU backward from dm: the up accumulator goes through the same
+      // staging area after the gate values have been read out.
+      float ub[PERL][8];
+      if constexpr (EPI == EPI_SWIGLU_BWD2) {
+        float gb[PERL][8];
+#pragma unroll
+        for (int q = 0; q < PERL; ++q) {
+          const int rr = (lane + 64 * q) / CH;
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(sW + rr * CPW + c8l);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(sW + rr * CPW + c8l + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            gb[q][e] = x0[e];
+            gb[q][4 + e] = x1[e];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            sW[(4 * (lane >> 4) + v) * CPW + 16 * j + (lane & 15)] = acc[1][i][j][v];
+#pragma unroll
+        for (int q = 0; q < PERL; ++q) {
+          const int rr = (lane + 64 * q) / CH;
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(sW + rr * CPW + c8l);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(sW + rr * CPW + c8l + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ub[q][e] = x0[e];
+            ub[q][4 + e] = x1[e];
+          }
+        }
+        // gate values back in place of the up values for the common read below
+#pragma unroll
+        for (int q = 0; q < PERL; ++q) {
+          const int rr = (lane + 64 * q) / CH;
+          *reinterpret_cast<f32x4*>(sW + rr * CPW + c8l) =
+              f32x4{gb[q][0], gb[q][1], gb[q][2], gb[q][3]};
+          *reinterpret_cast<f32x4*>(sW + rr * CPW + c8l + 4) =
+              f32x4{gb[q][4], gb[q][5], gb[q][6], gb[q][7]};
+        }
+      }
 #pragma unroll
       for (int q = 0; q < PERL; ++q) {
         const int id = lane + 64 * q;
@@ -552,6 +594,24 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
           gstore8<bf16_t>(static_cast<bf16_t*>(g.c[0]) + (int64_t)gr * g.ldc[0] + gcl, nvl, v);
         } else if constexpr (EPI == EPI_SWIGLU_BWD) {
           gstore8<bf16_t>(static_cast<bf16_t*>(g.c[o]) + (int64_t)gr * g.ldc[o] + gcl, nvl, v);
+        } else if constexpr (EPI == EPI_SWIGLU_BWD2) {
+          // v = g, ub = u, dm from the prefetched band inputs:
+          // m = SiLU(g) u; dg = dm u sig(g)(1 + g(1 - sig(g))); du = dm SiLU(g)
+          float dmv[8], mo[8], dgo[8], duo[8];
+          unpack16<bf16_t>(cur.r[q], dmv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float gg = v[e], uu = ub[q][e];
+            const float sg = sigmoid_f<bf16_t>(gg);
+            const float sl = gg * sg;
+            mo[e] = sl * uu;
+            dgo[e] = dmv[e] * uu * sg * (1.0f + gg * (1.0f - sg));
+            duo[e] = dmv[e] * sl;
+          }
+          const int64_t off = (int64_t)gr * g.ldc[0] + gcl;
+          gstore8<bf16_t>(static_cast<bf16_t*>(g.c[0]) + off, nvl, mo);
+          gstore8<bf16_t>(static_cast<bf16_t*>(g.c[1]) + (int64_t)gr * g.ldc[1] + gcl, nvl, dgo);
+          gstore8<bf16_t>(static_cast<bf16_t*>(g.c[2]) + (int64_t)gr * g.ldc[2] + gcl, nvl, duo);
         } else if constexpr (EPI == EPI_RMSBWD) {
           float hv[8], rv[8];
           unpack16<bf16_t>(cur.h[q], hv);

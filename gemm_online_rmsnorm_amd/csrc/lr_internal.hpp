@@ -17,7 +17,8 @@ enum GemmOp : int {
   OP_NN_STORE = 4,    // Y = X W [/ rowdiv] [+ res]             (grouped)
   OP_NN_RMSBWD = 5,   // RMSNorm backward epilogue + column sums
   OP_TN_WGRAD = 6,    // fp32 Y = X^T W [* colscale]            (grouped)
-  OP_COUNT = 7,
+  OP_SWIGLU_BWD2 = 7, // NT, NT pairs (g, u) + dm from res -> m, dg, du (pipelined engine)
+  OP_COUNT = 8,
 };
 
 struct GemmDesc {

@@ -186,7 +186,8 @@ static bool eligible2(int op, const GemmDesc& d, int groups, int bk) {
     case OP_NN_RMSBWD: mc = 2u; break;
     case OP_TN_WGRAD: mc = 3u; break;
     case OP_SWIGLU_BWD: mc = 32u; npair = 3; break;
-    case OP_NT_SWIGLU: npair = 2; break;
+    case OP_NT_SWIGLU:
+    case OP_SWIGLU_BWD2: npair = 2; break;
     default: break;
   }
   const int nsl = (npair == 1) ? groups : npair;
@@ -267,12 +268,16 @@ static hipError_t run_gemm2(int op, const GemmDesc& d, int groups, hipStream_t s
       if (ntiles(d, 256, 128, 1) >= kCUs) return launch2<P2x256x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
       return launch2<P2x128x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
     case OP_SWIGLU_BWD: return launch2<P3x128x128, 3, 32u, EPI_SWIGLU_BWD>(d, 1, s);
+    case OP_SWIGLU_BWD2:
+      if (ntiles(d, 256, 128, 1) >= kCUs)
+        return launch2<P2x256x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
+      return launch2<P2x128x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 static int engine2_bk(int op) {
-  return (op == OP_NT_SWIGLU || op == OP_SWIGLU_BWD) ? 32 : 64;
+  return (op == OP_NT_SWIGLU || op == OP_SWIGLU_BWD || op == OP_SWIGLU_BWD2) ? 32 : 64;
 }
 
 static bool g_engine2 = true;
@@ -280,7 +285,7 @@ static bool g_engine2 = true;
 void set_engine2(bool on) { g_engine2 = on; }
 
 int gemm2_tile_m(int op, const GemmDesc& d, int groups) {
-  if (op == OP_NT_SWIGLU) return ntiles(d, 256, 128, 1) >= kCUs ? 256 : 128;
+  if (op == OP_NT_SWIGLU || op == OP_SWIGLU_BWD2) return ntiles(d, 256, 128, 1) >= kCUs ? 256 : 128;
   if (op == OP_SWIGLU_BWD) return 128;
   return single_tile(d, groups) == 2 ? 128 : 256;
 }
@@ -356,6 +361,7 @@ hipError_t run_wgrad(int dtype, const GemmDesc& d, int groups, void* part, size_
 
 hipError_t run_gemm(int op, int dtype, const GemmDesc& d, int groups, hipStream_t s) {
   if (uses_engine2(op, dtype, d, groups)) return run_gemm2(op, d, groups, s);
+  if (op == OP_SWIGLU_BWD2) return hipErrorInvalidValue;  // pipelined engine only
   if (dtype == 0) return dispatch<float, TF32, TF32, TF32>(op, d, groups, s);
   return dispatch<bf16_t, TBig, TMid, TMid>(op, d, groups, s);
 }

@@ -38,8 +38,15 @@ def kernel_work(T: int, d: int, r: int, F: int, elem: int = 2, partials: bool = 
     # backward
     g("dB_dn", d, r, T, out_elem=4)
     g("dd_r", T, r, d)
-    W["SwiGLU recompute + backward"] = (3 * 2.0 * T * F * r,
-                                        e * (3 * T * r + 3 * F * r + 3 * T * F))
+    if e == 2:
+        # dm = dd_r A_dn, then g, u recomputed with m, dg, du from dm in the epilogue
+        g("dm = dd_r A_dn", T, F, r)
+        W["SwiGLU recompute + backward"] = (2 * 2.0 * T * F * r,
+                                            e * (2 * T * r + 2 * F * r + 4 * T * F))
+    else:
+        # fp32: one tile with three accumulators (g, u, dm)
+        W["SwiGLU recompute + backward"] = (3 * 2.0 * T * F * r,
+                                            e * (3 * T * r + 3 * F * r + 3 * T * F))
     g("dA_dn", r, F, T, out_elem=4)
     W["dB_g, dB_u"] = (2 * 2.0 * F * r * T, 2 * (e * (T * F + T * r) + 4 * F * r))
     W["dgu_r"] = (2 * 2.0 * T * r * F, 2 * e * (T * F + F * r + T * r) + 4 * T)
