@@ -1,6 +1,6 @@
 // Pipelined bf16 MFMA GEMM engine for gfx950 (the path for aligned shapes).
 //
-// Operand tiles go from HBM straight into LDS with global_load_lds_dwordx4
+// Operand tiles go from HBM straight into LDS with buffer_load_dwordx4 ... lds
 // (16 bytes per lane; a wave's instruction fills one contiguous 1 KB block),
 // through a ring of NSTAGE LDS stages: the loads of K-tile kt + NSTAGE - 1
 // are issued while K-tile kt is multiplied, and one barrier per K-tile
@@ -62,6 +62,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// The compiler schedules no instruction across this point.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// A value that is the same in every lane of a wave, moved to a scalar register.
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// 32-bit LDS address of a pointer into the kernel's shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Wait until every LDS read of this wave has returned its data. The
+// builtin (not inline asm) lets the compiler's own wait insertion see it.
+// Encoding: vmcnt = 63 (bits 3:0 and 15:14), expcnt = 7, lgkmcnt = 0.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // ---------------------------------------------------------------------------
 // One operand's DMA loader and fragment reader.
 //   R   rows of the operand tile (BM for A, BN for B)
@@ -82,7 +98,18 @@ struct Opnd {
   static constexpr int KPB = KC ? 1 : 64 / CPK;
   static_assert(KC || (R >= 128 && 64 % CPK == 0) || (KC), "M-contiguous tiles need R >= 128");
 
-  int32_t off[PER];  // per-lane element offsets of the loads (tile origin, k0 = 0)
+  // For M-contiguous tiles whose loads step through k-rows by a multiple of
+  // 16, every load of a lane has the same chunk swizzle and clamped column:
+  // one per-lane offset serves them all, the load index going into the
+  // scalar offset. This keeps vector registers free for the fragments.
+  static constexpr bool ONE_OFF = !KC && (NWAVE * KPB) % 16 == 0;
+  uint32_t off[ONE_OFF ? 1 : PER];  // per-lane byte offsets (tile origin, k0 = 0)
+  uint32_t vstep;                    // ONE_OFF: bytes between consecutive loads
+
+  // Elements from the operand's first element to one past its last one.
+  __device__ static __forceinline__ int64_t extent(int64_t ld, int Rtot, int K) {
+    return KC ? (int64_t)(Rtot - 1) * ld + K : (int64_t)(K - 1) * ld + Rtot;
+  }
 
   // Swizzle of a K-contiguous row: flips the chunk index so that 16
   // consecutive rows at one logical chunk hit 16 distinct bank groups.
@@ -93,16 +120,18 @@ struct Opnd {
   __device__ static __forceinline__ int swz_mc(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
 
   __device__ __forceinline__ void init(int64_t ld, int r0, int Rtot, int lane, int wave) {
+    vstep = (uint32_t)(2 * (int64_t)NWAVE * KPB * ld);
 #pragma unroll
-    for (int v = 0; v < PER; ++v) {
+    for (int v = 0; v < (ONE_OFF ? 1 : PER); ++v) {
       const int b = v * NWAVE + wave;
+      int64_t e;
       if constexpr (KC) {
         const int row = b * RPB + lane / CPR;
         const int pc = lane % CPR;
         const int c = pc ^ swz_kc(row);
         int gr = r0 + row;
         gr = gr < Rtot ? gr : Rtot - 1;
-        off[v] = (int32_t)((int64_t)gr * ld + 8 * c);
+        e = (int64_t)gr * ld + 8 * c;
       } else {
         const int k = b * KPB + lane / CPK;
         const int pc = lane % CPK;
@@ -110,19 +139,37 @@ struct Opnd {
         int gc = r0 / 8 + c;
         const int last = Rtot / 8 - 1;
         gc = gc < last ? gc : last;
-        off[v] = (int32_t)((int64_t)k * ld + 8 * gc);
+        e = (int64_t)k * ld + 8 * gc;
       }
+      off[v] = (uint32_t)(2 * e);
     }
   }
 
   // Issue this stage's loads: `src` points at the tile's k0 (element (r, k0)
-  // for KC, (k0, r) for MC), `dst` at the stage's LDS tile.
-  __device__ __forceinline__ void issue(const bf16_t* src, unsigned char* dst, int wave) const {
+  // for KC, (k0, r) for MC) and `nbytes` bytes from it are the operand's;
+  // `dst` is the stage's LDS tile. The loads go through a buffer resource
+  // (base and size in scalar registers, one 32-bit offset per lane): a lane
+  // whose offset fell outside [0, nbytes) would read zeros, never memory
+  // beyond the operand.
+  __device__ __forceinline__ void issue(const bf16_t* src, uint32_t nbytes, unsigned char* dst,
+                                        int wave) const {
+    // The buffer-resource type exists only for the GPU target; the host
+    // pass (which emits the launch stubs) must not see it.
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(src), (short)0, (int)nbytes, 0x00020000);
 #pragma unroll
     for (int v = 0; v < PER; ++v) {
       const int b = v * NWAVE + wave;
-      __builtin_amdgcn_global_load_lds(LR_GPTR(src + off[v]), LR_LPTR(dst + b * 1024), 16, 0, 0);
+      if constexpr (ONE_OFF)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LR_LPTR(dst + b * 1024), 16, off[0],
+                                                 v * vstep, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LR_LPTR(dst + b * 1024), 16, off[v], 0, 0, 0);
     }
+#else
+    (void)src; (void)nbytes; (void)dst; (void)wave;
+#endif
   }
 
   // Per-lane byte offsets of fragment reads inside a stage tile, for the
@@ -147,11 +194,14 @@ struct Opnd {
     } else {
       // The second read is 4 k-rows further down; its swizzle is the same
       // (k & 3 and (k >> 3) & 1 do not change when k grows by 4 within a
-      // lane's 8-row group).
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) bf16x4*)(tile + off));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) bf16x4*)(tile + off + 4 * R * 2));
+      // lane's 8-row group). The reads are issued as inline assembly: the
+      // compiler would otherwise make each wait for every pending
+      // HBM-to-LDS load, which serialises the pipeline. The caller waits
+      // for them (wait_lgkmcnt0) before the fragments are used.
+      const uint32_t a = lds_addr(tile + off);
+      bf16x4 lo, hi;
+      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a));
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(a), "n"(4 * R * 2));
       u32x4 r;
       r[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
       r[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3));
@@ -195,7 +245,9 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   float* sSS = reinterpret_cast<float*>(lds + BODY);  // [8][BM]
   float* sRow = sSS + 8 * BM;                          // [BM]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform across a wave: keep it in a scalar register.
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
   const int wm = wave / TL::NWN, wn = wave % TL::NWN;
   int tm, tn;
   tile_coords(g.tiles_m, g.tiles_n, tm, tn);
@@ -219,12 +271,15 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   const bf16_t* pa[3];
   const bf16_t* pb[3];
   int64_t sa[3], sb[3];  // element step of the source pointer per K-tile
+  int64_t ea[3], eb[3];  // elements of the operand from pa / pb on
   {
     const int p0 = slot;
     pa[0] = static_cast<const bf16_t*>(g.a[p0]);
     pb[0] = static_cast<const bf16_t*>(g.b[p0]);
     a0.init(g.lda[p0], m0, M, lane, wave);
     b0.init(g.ldb[p0], n0, N, lane, wave);
+    ea[0] = OA0::extent(g.lda[p0], M, g.K);
+    eb[0] = OB0::extent(g.ldb[p0], N, g.K);
     sa[0] = (MCMASK & 1u) ? (int64_t)BK * g.lda[p0] : BK;
     sb[0] = (MCMASK & 2u) ? (int64_t)BK * g.ldb[p0] : BK;
     if constexpr (NPAIR > 1) {
@@ -232,6 +287,8 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       pb[1] = static_cast<const bf16_t*>(g.b[1]);
       a1.init(g.lda[1], m0, M, lane, wave);
       b1.init(g.ldb[1], n0, N, lane, wave);
+      ea[1] = OA1::extent(g.lda[1], M, g.K);
+      eb[1] = OB1::extent(g.ldb[1], N, g.K);
       sa[1] = (MCMASK & 4u) ? (int64_t)BK * g.lda[1] : BK;
       sb[1] = (MCMASK & 8u) ? (int64_t)BK * g.ldb[1] : BK;
     }
@@ -240,6 +297,8 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       pb[2] = static_cast<const bf16_t*>(g.b[2]);
       a2.init(g.lda[2], m0, M, lane, wave);
       b2.init(g.ldb[2], n0, N, lane, wave);
+      ea[2] = OA2::extent(g.lda[2], M, g.K);
+      eb[2] = OB2::extent(g.ldb[2], N, g.K);
       sa[2] = (MCMASK & 16u) ? (int64_t)BK * g.lda[2] : BK;
       sb[2] = (MCMASK & 32u) ? (int64_t)BK * g.ldb[2] : BK;
     }
@@ -250,20 +309,23 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     for (int p = 0; p < NPAIR; ++p) {
       pa[p] += kt0 * sa[p];
       pb[p] += kt0 * sb[p];
+      ea[p] -= kt0 * sa[p];
+      eb[p] -= kt0 * sb[p];
     }
   }
   auto stage_ptr = [&](int s) { return lds + s * SB; };
   auto issue = [&](int kt) {
     unsigned char* st = stage_ptr(kt % S);
-    a0.issue(pa[0] + kt * sa[0], st, wave);
-    b0.issue(pb[0] + kt * sb[0], st + BM * BK * 2, wave);
+    auto nb = [&](int64_t e, int64_t step) { return (uint32_t)(2 * (e - kt * step)); };
+    a0.issue(pa[0] + kt * sa[0], nb(ea[0], sa[0]), st, wave);
+    b0.issue(pb[0] + kt * sb[0], nb(eb[0], sb[0]), st + BM * BK * 2, wave);
     if constexpr (NPAIR > 1) {
-      a1.issue(pa[1] + kt * sa[1], st + (BM + BN) * BK * 2, wave);
-      b1.issue(pb[1] + kt * sb[1], st + (2 * BM + BN) * BK * 2, wave);
+      a1.issue(pa[1] + kt * sa[1], nb(ea[1], sa[1]), st + (BM + BN) * BK * 2, wave);
+      b1.issue(pb[1] + kt * sb[1], nb(eb[1], sb[1]), st + (2 * BM + BN) * BK * 2, wave);
     }
     if constexpr (NPAIR > 2) {
-      a2.issue(pa[2] + kt * sa[2], st + 2 * (BM + BN) * BK * 2, wave);
-      b2.issue(pb[2] + kt * sb[2], st + (3 * BM + 2 * BN) * BK * 2, wave);
+      a2.issue(pa[2] + kt * sa[2], nb(ea[2], sa[2]), st + 2 * (BM + BN) * BK * 2, wave);
+      b2.issue(pb[2] + kt * sb[2], nb(eb[2], sb[2]), st + (3 * BM + 2 * BN) * BK * 2, wave);
     }
   };
   constexpr int L = OA0::PER + OB0::PER + (NPAIR > 1 ? OA1::PER + OB1::PER : 0) +
@@ -281,20 +343,70 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   // Per-lane fragment offsets (k-step 0; step 1 adds a constant).
   const int w0m = wm * TL::WTM, w0n = wn * TL::WTN;
 
-  float ssp[FM];
+  // Online RMSNorm: the waves of one row band (same wm) read the same A
+  // fragments; wave wn sums the squares of fragments i = wn, wn + NWN, ...
+  constexpr int FSS = (FM + TL::NWN - 1) / TL::NWN;
+  float ssp[FSS];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) ssp[i] = 0.f;
+  for (int i = 0; i < FSS; ++i) ssp[i] = 0.f;
   int panel = 0, in_panel = 0;
 
-  const int nk = g.ktiles_split;
+  // Fragment registers are double-buffered: the LDS reads of sub-step q + 1
+  // (a sub-step is one 32-wide k step of one operand pair) are in flight
+  // while the MFMAs of sub-step q run. The stage barrier sits before the
+  // last sub-step of a K-tile, once its fragments are in registers, so the
+  // first fragments of the next K-tile load under that sub-step's MFMAs.
+  constexpr int Q = NPAIR * TL::NSTEP;
+  u32x4 fa[2][FM], fb[2][FN];
+  auto read_q = [&](const unsigned char* st, int q, int buf) {
+    const int p = q / TL::NSTEP, s = q % TL::NSTEP;
+    const unsigned char* tA = st + p * (BM + BN) * BK * 2;
+    const unsigned char* tB = tA + BM * BK * 2;
+    const bool amc = (MCMASK >> (2 * p)) & 1u;
+    const bool bmc = (MCMASK >> (2 * p + 1)) & 1u;
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < nk) issue(s);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // Stage kt is complete when at most (stages issued after it) x L loads
-    // of this lane remain.
-    const int after = min(nk - 1 - kt, S - 2);
+    for (int i = 0; i < FM; ++i) {
+      if (amc)
+        fa[buf][i] = Opnd<BM, BK, TL::NWAVE, false>::read_frag(
+            tA, Opnd<BM, BK, TL::NWAVE, false>::frag_off(w0m + 16 * i, s, lane));
+      else
+        fa[buf][i] = Opnd<BM, BK, TL::NWAVE, true>::read_frag(
+            tA, Opnd<BM, BK, TL::NWAVE, true>::frag_off(w0m + 16 * i, s, lane));
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      if (bmc)
+        fb[buf][j] = Opnd<BN, BK, TL::NWAVE, false>::read_frag(
+            tB, Opnd<BN, BK, TL::NWAVE, false>::frag_off(w0n + 16 * j, s, lane));
+      else
+        fb[buf][j] = Opnd<BN, BK, TL::NWAVE, true>::read_frag(
+            tB, Opnd<BN, BK, TL::NWAVE, true>::frag_off(w0n + 16 * j, s, lane));
+    }
+  };
+  auto compute_q = [&](int q, int buf) {
+    const int p = q / TL::NSTEP;
+    if constexpr (ORMS) {
+      if (p == 0) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          if (i % TL::NWN == wn) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float lo = bf16_lo(fa[buf][i][c]), hi = bf16_hi(fa[buf][i][c]);
+              ssp[i / TL::NWN] = __builtin_fmaf(lo, lo, ssp[i / TL::NWN]);
+              ssp[i / TL::NWN] = __builtin_fmaf(hi, hi, ssp[i / TL::NWN]);
+            }
+          }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) mfma_step<bf16_t>(fa[buf][i], fb[buf][j], acc[p][i][j]);
+  };
+  // K-tile kt has landed in LDS when at most (K-tiles issued after it) x L
+  // loads of this lane remain; `after` is that count of K-tiles.
+  auto wait_tile = [&](int after) {
     if constexpr (S >= 4) {
       if (after >= 2) wait_vmcnt<2 * L>();
       else if (after == 1) wait_vmcnt<L>();
@@ -305,72 +417,74 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     } else {
       wait_vmcnt<0>();
     }
-    block_barrier();
-    if (kt + S - 1 < nk) issue(kt + S - 1);
+  };
 
+  const int nk = g.ktiles_split;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s);
+  wait_tile(min(nk - 1, S - 2));
+  block_barrier();
+  if (S - 1 < nk) issue(S - 1);
+  read_q(stage_ptr(0), 0, 0);
+
+  for (int kt = 0; kt < nk; ++kt) {
     const unsigned char* st = stage_ptr(kt % S);
 #pragma unroll
-    for (int p = 0; p < NPAIR; ++p) {
-      const unsigned char* tA = st + p * (BM + BN) * BK * 2;
-      const unsigned char* tB = tA + BM * BK * 2;
-#pragma unroll
-      for (int s = 0; s < TL::NSTEP; ++s) {
-        u32x4 af[FM], bfr[FN];
-        const bool amc = (MCMASK >> (2 * p)) & 1u;
-        const bool bmc = (MCMASK >> (2 * p + 1)) & 1u;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          if (amc)
-            af[i] = Opnd<BM, BK, TL::NWAVE, false>::read_frag(
-                tA, Opnd<BM, BK, TL::NWAVE, false>::frag_off(w0m + 16 * i, s, lane));
-          else
-            af[i] = Opnd<BM, BK, TL::NWAVE, true>::read_frag(
-                tA, Opnd<BM, BK, TL::NWAVE, true>::frag_off(w0m + 16 * i, s, lane));
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          if (bmc)
-            bfr[j] = Opnd<BN, BK, TL::NWAVE, false>::read_frag(
-                tB, Opnd<BN, BK, TL::NWAVE, false>::frag_off(w0n + 16 * j, s, lane));
-          else
-            bfr[j] = Opnd<BN, BK, TL::NWAVE, true>::read_frag(
-                tB, Opnd<BN, BK, TL::NWAVE, true>::frag_off(w0n + 16 * j, s, lane));
-        }
-        if constexpr (ORMS) {
-          if (p == 0 && wn == 0) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const float lo = bf16_lo(af[i][q]), hi = bf16_hi(af[i][q]);
-                ssp[i] = __builtin_fmaf(lo, lo, ssp[i]);
-                ssp[i] = __builtin_fmaf(hi, hi, ssp[i]);
-              }
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) mfma_step<bf16_t>(af[i], bfr[j], acc[p][i][j]);
+    for (int q = 0; q < Q; ++q) {
+      const int buf = q & 1;
+      // Nothing is scheduled across this wait in either direction: the
+      // fragments of sub-step q (some read by inline assembly the compiler
+      // does not track) are in registers only after it.
+      sched_fence();
+      wait_lgkmcnt0();
+      sched_fence();
+      if (q + 1 < Q) {
+        read_q(st, q + 1, buf ^ 1);
+      } else if (kt + 1 < nk) {
+        // Every wave has its fragments of K-tile kt in registers once it
+        // passes the barrier; the stage of K-tile kt is then free for
+        // K-tile kt + S, and K-tile kt + 1 has landed.
+        wait_tile(min(nk - 2 - kt, S - 2));
+        block_barrier();
+        if (kt + S < nk) issue(kt + S);
+        read_q(stage_ptr((kt + 1) % S), 0, buf ^ 1);
       }
+      compute_q(q, buf);
+    }
+    if constexpr (Q & 1) {
+      // An odd sub-step count leaves the next K-tile's first fragments in
+      // buffer 1; the loop reads sub-step 0 from buffer 0. The copy waits
+      // for the reads to land.
+      sched_fence();
+      wait_lgkmcnt0();
+      sched_fence();
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[0][i] = fa[1][i];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[0][j] = fb[1][j];
     }
     if constexpr (ORMS) {
       if (++in_panel == g.panel_ktiles || kt == nk - 1) {
-        if (wn == 0) {
 #pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            float x = ssp[i];
+        for (int i = 0; i < FM; ++i)
+          if (i % TL::NWN == wn) {
+            float x = ssp[i / TL::NWN];
             x += __shfl_xor(x, 16, 64);
             x += __shfl_xor(x, 32, 64);
             if (lane < 16) sSS[panel * BM + w0m + 16 * i + lane] = x;
-            ssp[i] = 0.f;
+            ssp[i / TL::NWN] = 0.f;
           }
-        }
         ++panel;
         in_panel = 0;
       }
     }
   }
+  // With no K-tile at all the fragments read before the loop are still in
+  // flight; nothing may reuse their registers before they land.
+  sched_fence();
+  wait_lgkmcnt0();
+  sched_fence();
   __syncthreads();  // every wave is done with the ring; sSS is visible
 
   if constexpr (ORMS) {

@@ -177,6 +177,11 @@ static int64_t ntiles(const GemmDesc& d, int bm, int bn, int groups) {
 // Whether the pipelined engine can run this GEMM: k-tiles divide K, the
 // M/N-contiguous operands have whole 8-element chunks, every per-lane load
 // offset fits in 32 bits, and the Online RMSNorm panels are whole k-tiles.
+// Elements from an operand's first element to one past its last one.
+static int64_t operand_extent(bool mc, int64_t ld, int rows, int K) {
+  return mc ? (int64_t)(K - 1) * ld + rows : (int64_t)(rows - 1) * ld + K;
+}
+
 static bool eligible2(int op, const GemmDesc& d, int groups, int bk) {
   if (d.K % bk != 0 || d.M < 1 || d.N < 1) return false;
   uint32_t mc = 0;
@@ -194,10 +199,12 @@ static bool eligible2(int op, const GemmDesc& d, int groups, int bk) {
   for (int p = 0; p < nsl; ++p) {
     const int lp = (npair == 1) ? 0 : p;  // the groups of a grouped GEMM share pair 0's layout
     const bool amc = (mc >> (2 * lp)) & 1u, bmc = (mc >> (2 * lp + 1)) & 1u;
-    if (amc ? (d.M % 8 != 0) : ((int64_t)d.M * d.lda[p] >= ((int64_t)1 << 31))) return false;
-    if (bmc ? (d.N % 8 != 0) : ((int64_t)d.N * d.ldb[p] >= ((int64_t)1 << 31))) return false;
-    if (amc && (int64_t)bk * d.lda[p] >= ((int64_t)1 << 31)) return false;
-    if (bmc && (int64_t)bk * d.ldb[p] >= ((int64_t)1 << 31)) return false;
+    // M/N-contiguous tiles need whole 16-byte row chunks; every operand's
+    // byte extent must fit the 32-bit offsets of a buffer resource.
+    if (amc && d.M % 8 != 0) return false;
+    if (bmc && d.N % 8 != 0) return false;
+    if (operand_extent(amc, d.lda[p], d.M, d.K) >= ((int64_t)1 << 31)) return false;
+    if (operand_extent(bmc, d.ldb[p], d.N, d.K) >= ((int64_t)1 << 31)) return false;
   }
   if (op == OP_NT_ORMS && d.n_panels > 1 && d.panel_width % bk != 0) return false;
   return true;
