@@ -8,9 +8,13 @@
 // way to LDS. Both operand storage orders are consumed directly:
 //
 //  * K-contiguous operands ([rows][k]) sit in LDS as rows of BK elements.
-//    The 16-byte chunks of a row are XOR-swizzled so that the 16 lanes of
-//    an MFMA fragment read (16 consecutive rows, one chunk) hit 16 distinct
-//    4-bank groups. Fragments are read with ds_read_b128.
+//    The 16-byte chunks of a row are XOR-swizzled so that the lanes of an
+//    MFMA fragment read (consecutive rows, one chunk) spread over distinct
+//    4-bank groups: chunk ^ ((row >> 1) & 7) for 128-byte rows (BK = 64),
+//    chunk ^ ((row >> 1) & 3) for 64-byte rows (BK = 32). For the latter the
+//    LDS bank-conflict counters read 47% with the 16-row pattern
+//    chunk ^ ((row >> 2) & 3) and 5% with this 8-row one. Fragments are read
+//    with ds_read_b128.
 //  * M/N-contiguous operands ([k][rows]) sit in LDS as k-rows; fragments are
 //    read with ds_read_b64_tr_b16, the transposing LDS read: within a
 //    16-lane group, result lane i element e is element (i & 3) of the
@@ -68,6 +72,26 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // A value that is the same in every lane of a wave, moved to a scalar register.
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Scheduling hint for one sub-step: NVM HBM-to-LDS loads, then NDS
+// fragment reads, each followed by an equal share of the NMF MFMAs, then
+// the rest of the MFMAs. One memory instruction between every few MFMAs
+// keeps the memory queues short and the matrix pipe busy.
+template <int NDS, int NVM, int NMF>
+__device__ __forceinline__ void interleave() {
+  constexpr int per = (NDS + NVM) ? NMF / (NDS + NVM) : 0;
+#pragma unroll
+  for (int k = 0; k < NVM; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+    __builtin_amdgcn_sched_group_barrier(0x008, per, 0);  // MFMA
+  }
+#pragma unroll
+  for (int k = 0; k < NDS; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, per, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NMF - (NDS + NVM) * per, 0);
+}
+
 // 32-bit LDS address of a pointer into the kernel's shared memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -111,10 +135,10 @@ struct Opnd {
     return KC ? (int64_t)(Rtot - 1) * ld + K : (int64_t)(K - 1) * ld + Rtot;
   }
 
-  // Swizzle of a K-contiguous row: flips the chunk index so that 16
-  // consecutive rows at one logical chunk hit 16 distinct bank groups.
+  // Swizzle of a K-contiguous row: flips the chunk index so that
+  // consecutive rows at one logical chunk hit distinct bank groups.
   __device__ static __forceinline__ int swz_kc(int row) {
-    return (BK == 64) ? ((row >> 1) & 7) : ((row >> 2) & 3);
+    return (BK == 64) ? ((row >> 1) & 7) : ((row >> 1) & 3);
   }
   // Swizzle of a k-row of an M-contiguous tile (flips chunk bits 1..3).
   __device__ static __forceinline__ int swz_mc(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
@@ -316,7 +340,11 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   auto stage_ptr = [&](int s) { return lds + s * SB; };
   auto issue = [&](int kt) {
     unsigned char* st = stage_ptr(kt % S);
-    auto nb = [&](int64_t e, int64_t step) { return (uint32_t)(2 * (e - kt * step)); };
+    // A K-tile past the last one loads nothing: an empty buffer range
+    // reads zeros without touching memory, so the loop issues its loads
+    // without branches.
+    const bool live = kt < g.ktiles_split;
+    auto nb = [&](int64_t e, int64_t step) { return live ? (uint32_t)(2 * (e - kt * step)) : 0u; };
     a0.issue(pa[0] + kt * sa[0], nb(ea[0], sa[0]), st, wave);
     b0.issue(pb[0] + kt * sb[0], nb(eb[0], sb[0]), st + BM * BK * 2, wave);
     if constexpr (NPAIR > 1) {
@@ -406,27 +434,29 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   };
   // K-tile kt has landed in LDS when at most (K-tiles issued after it) x L
   // loads of this lane remain; `after` is that count of K-tiles.
-  auto wait_tile = [&](int after) {
-    if constexpr (S >= 4) {
-      if (after >= 2) wait_vmcnt<2 * L>();
-      else if (after == 1) wait_vmcnt<L>();
-      else wait_vmcnt<0>();
-    } else if constexpr (S == 3) {
-      if (after >= 1) wait_vmcnt<L>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();
-    }
-  };
+  // Every K-tile index is issued (past the last one with an empty range),
+  // so K-tile kt has landed once at most (S - 2) x L loads of this lane
+  // are in flight.
+  constexpr int VM_AFTER = (S - 2) * L;
+  // DS reads of one sub-step of pair 0 (K-contiguous fragments; the
+  // transposing reads of M-contiguous ones are inline assembly the
+  // scheduler cannot group).
+  constexpr int NDS = ((MCMASK & 1u) ? 0 : FM) + ((MCMASK & 2u) ? 0 : FN);
 
   const int nk = g.ktiles_split;
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < nk) issue(s);
-  wait_tile(min(nk - 1, S - 2));
+  for (int s = 0; s < S - 1; ++s) issue(s);
+  wait_vmcnt<VM_AFTER>();
   block_barrier();
-  if (S - 1 < nk) issue(S - 1);
+  issue(S - 1);
   read_q(stage_ptr(0), 0, 0);
+  // Fragment reads are in flight only inside the loop body, between a
+  // sub-step's start and the next sub-step's wait: every path into and out
+  // of the loop has them landed, so code the compiler places at the loop's
+  // edges cannot touch registers still being written.
+  sched_fence();
+  wait_lgkmcnt0();
+  sched_fence();
 
   for (int kt = 0; kt < nk; ++kt) {
     const unsigned char* st = stage_ptr(kt % S);
@@ -441,16 +471,20 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       sched_fence();
       if (q + 1 < Q) {
         read_q(st, q + 1, buf ^ 1);
-      } else if (kt + 1 < nk) {
+        compute_q(q, buf);
+        interleave<NDS, 0, FM * FN>();
+      } else {
         // Every wave has its fragments of K-tile kt in registers once it
         // passes the barrier; the stage of K-tile kt is then free for
-        // K-tile kt + S, and K-tile kt + 1 has landed.
-        wait_tile(min(nk - 2 - kt, S - 2));
+        // K-tile kt + S, and K-tile kt + 1 has landed. (On the last K-tile
+        // this reads a stage no MFMA uses.)
+        wait_vmcnt<VM_AFTER>();
         block_barrier();
-        if (kt + S < nk) issue(kt + S);
+        issue(kt + S);
         read_q(stage_ptr((kt + 1) % S), 0, buf ^ 1);
+        compute_q(q, buf);
+        interleave<NDS, L, FM * FN>();
       }
-      compute_q(q, buf);
     }
     if constexpr (Q & 1) {
       // An odd sub-step count leaves the next K-tile's first fragments in
@@ -479,11 +513,17 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
         in_panel = 0;
       }
     }
+    sched_fence();
+    wait_lgkmcnt0();
+    sched_fence();
   }
-  // With no K-tile at all the fragments read before the loop are still in
-  // flight; nothing may reuse their registers before they land.
+  // The last fragment reads (of a stage no MFMA uses, or before the loop
+  // with no K-tile at all) and the empty-range loads past the last K-tile
+  // are still in flight; nothing may reuse their registers or LDS before
+  // they land.
   sched_fence();
   wait_lgkmcnt0();
+  wait_vmcnt<0>();
   sched_fence();
   __syncthreads();  // every wave is done with the ring; sSS is visible
 
