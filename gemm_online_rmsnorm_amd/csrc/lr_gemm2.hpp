@@ -44,10 +44,17 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #define LR_GPTR(p) ((__attribute__((address_space(1))) void*)(p))
 #define LR_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-template <int BM_, int BN_, int BK_, int NWM_, int NWN_, int NSTAGE_>
+// NSPLIT = 2: a two-pair tile whose B rows hold pair 0's BN / 2 rows, then
+// pair 1's; waves of the first NWN / 2 columns multiply pair 0, the others
+// pair 1. Each wave runs one pair, so the LDS reads per MFMA are those of a
+// one-pair tile twice the size; the epilogue pairs up the two halves.
+template <int BM_, int BN_, int BK_, int NWM_, int NWN_, int NSTAGE_, int NSPLIT_ = 1>
 struct Tile2 {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, NWM = NWM_, NWN = NWN_;
   static constexpr int NSTAGE = NSTAGE_;
+  static constexpr int NSPLIT = NSPLIT_;
+  static constexpr int BNO = BN / NSPLIT;  // output columns of a block tile
+  static_assert(NSPLIT == 1 || (NSPLIT == 2 && NWN % 2 == 0), "split tiles need an even NWN");
   static constexpr int NT = 64 * NWM * NWN;
   static constexpr int NWAVE = NWM * NWN;
   static constexpr int WTM = BM / NWM, WTN = BN / NWN;
@@ -92,6 +99,12 @@ __device__ __forceinline__ void interleave() {
   __builtin_amdgcn_sched_group_barrier(0x008, NMF - (NDS + NVM) * per, 0);
 }
 
+// Element i (0..2, the same in every lane) of a three-entry argument array.
+template <typename T>
+__device__ __forceinline__ T pick3(const T (&a)[3], int i) {
+  return i == 0 ? a[0] : (i == 1 ? a[1] : a[2]);
+}
+
 // 32-bit LDS address of a pointer into the kernel's shared memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -122,13 +135,14 @@ struct Opnd {
   static constexpr int KPB = KC ? 1 : 64 / CPK;
   static_assert(KC || (R >= 128 && 64 % CPK == 0) || (KC), "M-contiguous tiles need R >= 128");
 
-  // For M-contiguous tiles whose loads step through k-rows by a multiple of
-  // 16, every load of a lane has the same chunk swizzle and clamped column:
-  // one per-lane offset serves them all, the load index going into the
-  // scalar offset. This keeps vector registers free for the fragments.
-  static constexpr bool ONE_OFF = !KC && (NWAVE * KPB) % 16 == 0;
-  uint32_t off[ONE_OFF ? 1 : PER];  // per-lane byte offsets (tile origin, k0 = 0)
-  uint32_t vstep;                    // ONE_OFF: bytes between consecutive loads
+  // Consecutive loads of a lane step through rows (KC) or k-rows (MC) by
+  // VROWS, a multiple of the swizzle period, so every load of a lane has
+  // the same chunk swizzle and one per-lane offset serves them all; the
+  // load index moves the base of the buffer resource (KC) or goes into the
+  // scalar offset (MC). This keeps vector registers free for fragments.
+  static constexpr int VROWS = NWAVE * (KC ? RPB : KPB);
+  uint32_t off;    // per-lane byte offset of load 0 (tile origin, k0 = 0)
+  uint32_t vstep;  // bytes between consecutive loads of a lane
 
   // Elements from the operand's first element to one past its last one.
   __device__ static __forceinline__ int64_t extent(int64_t ld, int Rtot, int K) {
@@ -143,53 +157,59 @@ struct Opnd {
   // Swizzle of a k-row of an M-contiguous tile (flips chunk bits 1..3).
   __device__ static __forceinline__ int swz_mc(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
 
+  // K-contiguous rows past Rtot are not clamped: their offsets lie past the
+  // operand's extent, so the buffer range check returns zeros for them (they
+  // only feed outputs that are never stored). M-contiguous column chunks
+  // past Rtot are clamped to the last one.
   __device__ __forceinline__ void init(int64_t ld, int r0, int Rtot, int lane, int wave) {
-    vstep = (uint32_t)(2 * (int64_t)NWAVE * KPB * ld);
-#pragma unroll
-    for (int v = 0; v < (ONE_OFF ? 1 : PER); ++v) {
-      const int b = v * NWAVE + wave;
-      int64_t e;
-      if constexpr (KC) {
-        const int row = b * RPB + lane / CPR;
-        const int pc = lane % CPR;
-        const int c = pc ^ swz_kc(row);
-        int gr = r0 + row;
-        gr = gr < Rtot ? gr : Rtot - 1;
-        e = (int64_t)gr * ld + 8 * c;
-      } else {
-        const int k = b * KPB + lane / CPK;
-        const int pc = lane % CPK;
-        const int c = pc ^ swz_mc(k);
-        int gc = r0 / 8 + c;
-        const int last = Rtot / 8 - 1;
-        gc = gc < last ? gc : last;
-        e = (int64_t)k * ld + 8 * gc;
-      }
-      off[v] = (uint32_t)(2 * e);
+    static_assert(KC ? VROWS % (BK == 64 ? 16 : 8) == 0 : VROWS % 16 == 0,
+                  "loads of a lane must share their swizzle");
+    // The same in every lane; kept in a scalar register so the buffer
+    // resources built from it are scalar too.
+    vstep = (uint32_t)wave_uniform((int)(2 * (int64_t)VROWS * ld));
+    int64_t e;
+    if constexpr (KC) {
+      const int row = wave * RPB + lane / CPR;
+      const int c = (lane % CPR) ^ swz_kc(row);
+      e = (int64_t)(r0 + row) * ld + 8 * c;
+    } else {
+      const int k = wave * KPB + lane / CPK;
+      const int c = (lane % CPK) ^ swz_mc(k);
+      int gc = r0 / 8 + c;
+      const int last = Rtot / 8 - 1;
+      gc = gc < last ? gc : last;
+      e = (int64_t)k * ld + 8 * gc;
     }
+    off = (uint32_t)(2 * e);
   }
 
   // Issue this stage's loads: `src` points at the tile's k0 (element (r, k0)
   // for KC, (k0, r) for MC) and `nbytes` bytes from it are the operand's;
-  // `dst` is the stage's LDS tile. The loads go through a buffer resource
+  // `dst` is the stage's LDS tile. The loads go through buffer resources
   // (base and size in scalar registers, one 32-bit offset per lane): a lane
-  // whose offset fell outside [0, nbytes) would read zeros, never memory
-  // beyond the operand.
+  // whose offset falls outside the range reads zeros, never memory beyond
+  // the operand.
   __device__ __forceinline__ void issue(const bf16_t* src, uint32_t nbytes, unsigned char* dst,
                                         int wave) const {
     // The buffer-resource type exists only for the GPU target; the host
     // pass (which emits the launch stubs) must not see it.
 #if defined(__HIP_DEVICE_COMPILE__)
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(src), (short)0, (int)nbytes, 0x00020000);
 #pragma unroll
     for (int v = 0; v < PER; ++v) {
       const int b = v * NWAVE + wave;
-      if constexpr (ONE_OFF)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LR_LPTR(dst + b * 1024), 16, off[0],
-                                                 v * vstep, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LR_LPTR(dst + b * 1024), 16, off[v], 0, 0, 0);
+      if constexpr (KC) {
+        const uint32_t adv = (uint32_t)wave_uniform((int)((uint32_t)v * vstep));
+        const int rem = wave_uniform((int)(nbytes > adv ? nbytes - adv : 0u));
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<unsigned char*>(reinterpret_cast<const unsigned char*>(src)) + adv, (short)0,
+            rem, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LR_LPTR(dst + b * 1024), 16, off, 0, 0, 0);
+      } else {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16_t*>(src), (short)0, (int)nbytes, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LR_LPTR(dst + b * 1024), 16, off, v * vstep, 0,
+                                                 0);
+      }
     }
 #else
     (void)src; (void)nbytes; (void)dst; (void)wave;
@@ -238,7 +258,7 @@ struct Opnd {
 
 template <class TL, int NPAIR>
 constexpr int stage_bytes() {
-  return NPAIR * (TL::BM + TL::BN) * TL::BK * 2;
+  return (TL::NSPLIT == 2 ? 2 * TL::BM + TL::BN : NPAIR * (TL::BM + TL::BN)) * TL::BK * 2;
 }
 
 template <class TL>
@@ -261,6 +281,10 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, S = TL::NSTAGE;
   constexpr int FM = TL::FM, FN = TL::FN;
   constexpr bool ORMS = (EPI == EPI_ORMS);
+  constexpr bool SPLITN = (TL::NSPLIT == 2);
+  static_assert(!SPLITN || (NPAIR == 2 && MCMASK == 0u && !ORMS && EPI != EPI_RMSBWD),
+                "split tiles are for K-contiguous two-pair products");
+  constexpr int BNO = TL::BNO;
   constexpr int SB = stage_bytes<TL, NPAIR>();
   extern __shared__ __align__(16) unsigned char lds[];
   constexpr int RING = S * SB;
@@ -275,15 +299,15 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   const int wm = wave / TL::NWN, wn = wave % TL::NWN;
   int tm, tn;
   tile_coords(g.tiles_m, g.tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = tn * BNO;
   const int slot = (NPAIR == 1) ? (int)blockIdx.z % g.groups : 0;
   const int split = (int)blockIdx.z / g.groups;
   const int M = g.M, N = g.N;
 
   using OA0 = Opnd<BM, BK, TL::NWAVE, !(MCMASK & 1u)>;
-  using OB0 = Opnd<BN, BK, TL::NWAVE, !(MCMASK & 2u)>;
+  using OB0 = Opnd<BNO, BK, TL::NWAVE, !(MCMASK & 2u)>;
   using OA1 = Opnd<BM, BK, TL::NWAVE, !(MCMASK & 4u)>;
-  using OB1 = Opnd<BN, BK, TL::NWAVE, !(MCMASK & 8u)>;
+  using OB1 = Opnd<BNO, BK, TL::NWAVE, !(MCMASK & 8u)>;
   using OA2 = Opnd<BM, BK, TL::NWAVE, !(MCMASK & 16u)>;
   using OB2 = Opnd<BN, BK, TL::NWAVE, !(MCMASK & 32u)>;
   OA0 a0;
@@ -298,14 +322,18 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   int64_t ea[3], eb[3];  // elements of the operand from pa / pb on
   {
     const int p0 = slot;
-    pa[0] = static_cast<const bf16_t*>(g.a[p0]);
-    pb[0] = static_cast<const bf16_t*>(g.b[p0]);
-    a0.init(g.lda[p0], m0, M, lane, wave);
-    b0.init(g.ldb[p0], n0, N, lane, wave);
-    ea[0] = OA0::extent(g.lda[p0], M, g.K);
-    eb[0] = OB0::extent(g.ldb[p0], N, g.K);
-    sa[0] = (MCMASK & 1u) ? (int64_t)BK * g.lda[p0] : BK;
-    sb[0] = (MCMASK & 2u) ? (int64_t)BK * g.ldb[p0] : BK;
+    // Selected with constant indices (not g.a[p0]): a run-time index into
+    // the argument arrays would go through private memory, and the values
+    // would no longer be known to be the same in every lane.
+    pa[0] = static_cast<const bf16_t*>(pick3(g.a, p0));
+    pb[0] = static_cast<const bf16_t*>(pick3(g.b, p0));
+    const int64_t lda0 = pick3(g.lda, p0), ldb0 = pick3(g.ldb, p0);
+    a0.init(lda0, m0, M, lane, wave);
+    b0.init(ldb0, n0, N, lane, wave);
+    ea[0] = OA0::extent(lda0, M, g.K);
+    eb[0] = OB0::extent(ldb0, N, g.K);
+    sa[0] = (MCMASK & 1u) ? (int64_t)BK * lda0 : BK;
+    sb[0] = (MCMASK & 2u) ? (int64_t)BK * ldb0 : BK;
     if constexpr (NPAIR > 1) {
       pa[1] = static_cast<const bf16_t*>(g.a[1]);
       pb[1] = static_cast<const bf16_t*>(g.b[1]);
@@ -345,6 +373,14 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     // without branches.
     const bool live = kt < g.ktiles_split;
     auto nb = [&](int64_t e, int64_t step) { return live ? (uint32_t)(2 * (e - kt * step)) : 0u; };
+    if constexpr (SPLITN) {
+      // [A0][A1][B0][B1]: the two B tiles form one BN-row tile.
+      a0.issue(pa[0] + kt * sa[0], nb(ea[0], sa[0]), st, wave);
+      a1.issue(pa[1] + kt * sa[1], nb(ea[1], sa[1]), st + BM * BK * 2, wave);
+      b0.issue(pb[0] + kt * sb[0], nb(eb[0], sb[0]), st + 2 * BM * BK * 2, wave);
+      b1.issue(pb[1] + kt * sb[1], nb(eb[1], sb[1]), st + (2 * BM + BNO) * BK * 2, wave);
+      return;
+    }
     a0.issue(pa[0] + kt * sa[0], nb(ea[0], sa[0]), st, wave);
     b0.issue(pb[0] + kt * sb[0], nb(eb[0], sb[0]), st + BM * BK * 2, wave);
     if constexpr (NPAIR > 1) {
@@ -360,9 +396,10 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
                     (NPAIR > 2 ? OA2::PER + OB2::PER : 0);
   static_assert(L * (S - 1) < 64, "too many loads in flight for vmcnt");
 
-  f32x4 acc[NPAIR][FM][FN];
+  constexpr int NACC = SPLITN ? 1 : NPAIR;
+  f32x4 acc[NACC][FM][FN];
 #pragma unroll
-  for (int p = 0; p < NPAIR; ++p)
+  for (int p = 0; p < NACC; ++p)
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -370,6 +407,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
 
   // Per-lane fragment offsets (k-step 0; step 1 adds a constant).
   const int w0m = wm * TL::WTM, w0n = wn * TL::WTN;
+  const int pw = SPLITN ? wn / (TL::NWN / 2) : 0;  // the pair a split-tile wave runs
 
   // Online RMSNorm: the waves of one row band (same wm) read the same A
   // fragments; wave wn sums the squares of fragments i = wn, wn + NWN, ...
@@ -384,12 +422,12 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   // while the MFMAs of sub-step q run. The stage barrier sits before the
   // last sub-step of a K-tile, once its fragments are in registers, so the
   // first fragments of the next K-tile load under that sub-step's MFMAs.
-  constexpr int Q = NPAIR * TL::NSTEP;
+  constexpr int Q = (SPLITN ? 1 : NPAIR) * TL::NSTEP;
   u32x4 fa[2][FM], fb[2][FN];
   auto read_q = [&](const unsigned char* st, int q, int buf) {
     const int p = q / TL::NSTEP, s = q % TL::NSTEP;
-    const unsigned char* tA = st + p * (BM + BN) * BK * 2;
-    const unsigned char* tB = tA + BM * BK * 2;
+    const unsigned char* tA = SPLITN ? st + pw * BM * BK * 2 : st + p * (BM + BN) * BK * 2;
+    const unsigned char* tB = SPLITN ? st + 2 * BM * BK * 2 : tA + BM * BK * 2;
     const bool amc = (MCMASK >> (2 * p)) & 1u;
     const bool bmc = (MCMASK >> (2 * p + 1)) & 1u;
 #pragma unroll
@@ -548,31 +586,68 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  // Elementwise combination of the accumulators.
-  if constexpr (EPI == EPI_SWIGLU) {
+  // Split tiles: the wave running pair 0 (gate) and its partner in the same
+  // row band running pair 1 (up) each finish half of the bands, handing the
+  // other half of their accumulators over through LDS (the ring is free).
+  // Afterwards acc[0][i] holds the gate and acc[0][FME + i] the up values of
+  // band keep0 + i. LR_E(p, i, j) names pair p of epilogue band i.
+  constexpr int FME = SPLITN ? FM / 2 : FM;
+  const int keep0 = pw * FME;
+  const int rb = w0m + 16 * keep0;                                  // first row
+  const int cb = SPLITN ? (wn % (TL::NWN / 2)) * TL::WTN : w0n;  // first column
+  if constexpr (SPLITN) {
+    const int partner = wm * TL::NWN + (wn + TL::NWN / 2) % TL::NWN;
+    float* xch = reinterpret_cast<float*>(lds);  // [NWAVE][FME][FN][4][64]
+    static_assert(TL::NWAVE * FME * FN * 4 * 64 * 4 <= RING, "exchange area exceeds the ring");
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FME; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          xch[(((wave * FME + i) * FN + j) * 4 + v) * 64 + lane] =
+              pw ? acc[0][i][j][v] : acc[0][FME + i][j][v];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < FME; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float gg = acc[0][i][j][v];
-          acc[0][i][j][v] = gg * sigmoid_f<bf16_t>(gg) * acc[1][i][j][v];
+          const float other = xch[(((partner * FME + i) * FN + j) * 4 + v) * 64 + lane];
+          const float own = pw ? acc[0][FME + i][j][v] : acc[0][i][j][v];
+          acc[0][i][j][v] = pw ? other : own;
+          acc[0][FME + i][j][v] = pw ? own : other;
+        }
+    __syncthreads();  // the staging area below overlaps the exchange area
+  }
+#define LR_E(p, i, j) acc[SPLITN ? 0 : (p)][SPLITN ? (p) * FME + (i) : (i)][j]
+
+  // Elementwise combination of the accumulators.
+  if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < FME; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float gg = LR_E(0, i, j)[v];
+          LR_E(0, i, j)[v] = gg * sigmoid_f<bf16_t>(gg) * LR_E(1, i, j)[v];
         }
   }
   if constexpr (EPI == EPI_SWIGLU_BWD) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FME; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float gg = acc[0][i][j][v], uu = acc[1][i][j][v], dm = acc[2][i][j][v];
+          const float gg = LR_E(0, i, j)[v], uu = LR_E(1, i, j)[v], dm = LR_E(2, i, j)[v];
           const float sg = sigmoid_f<bf16_t>(gg);
           const float sl = gg * sg;
-          acc[0][i][j][v] = sl * uu;
-          acc[1][i][j][v] = dm * uu * sg * (1.0f + gg * (1.0f - sg));
-          acc[2][i][j][v] = dm * sl;
+          LR_E(0, i, j)[v] = sl * uu;
+          LR_E(1, i, j)[v] = dm * uu * sg * (1.0f + gg * (1.0f - sg));
+          LR_E(2, i, j)[v] = dm * sl;
         }
   }
 
@@ -592,7 +667,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   constexpr bool HAS_GAMMA = (EPI == EPI_RMSBWD || EPI == EPI_WGRAD);
   constexpr bool HAS_ROW = (EPI == EPI_STORE || EPI == EPI_RMSBWD);
   const int c8l = (lane % CH) * 8;             // this lane's column chunk in the band
-  const int gcl = n0 + w0n + c8l;              // its global column
+  const int gcl = n0 + cb + c8l;              // its global column
   const int nvl = N - gcl;                     // valid columns of the chunk
   const bool col_ok = gcl < N;
   float colacc[8];
@@ -617,7 +692,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
 #pragma unroll
     for (int q = 0; q < PERL; ++q) {
       const int rr = (lane + 64 * q) / CH;
-      const int gr = m0 + w0m + 16 * i + rr;
+      const int gr = m0 + rb + 16 * i + rr;
       const bool ok = col_ok && gr < M;
       in.r[q] = u32x4{0u, 0u, 0u, 0u};
       in.h[q] = u32x4{0u, 0u, 0u, 0u};
@@ -658,15 +733,15 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     BandIn cur, nxt;
     if constexpr (HAS_RES || HAS_ROW) load_band(0, cur);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FME; ++i) {
       if constexpr (HAS_RES || HAS_ROW) {
-        if (i + 1 < FM) load_band(i + 1, nxt);
+        if (i + 1 < FME) load_band(i + 1, nxt);
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          sW[(4 * (lane >> 4) + v) * CPW + 16 * j + (lane & 15)] = acc[ao][i][j][v];
+          sW[(4 * (lane >> 4) + v) * CPW + 16 * j + (lane & 15)] = LR_E(ao, i, j)[v];
       // SwiGLU backward from dm: the up accumulator goes through the same
       // staging area after the gate values have been read out.
       float ub[PERL][8];
@@ -687,7 +762,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
         for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            sW[(4 * (lane >> 4) + v) * CPW + 16 * j + (lane & 15)] = acc[1][i][j][v];
+            sW[(4 * (lane >> 4) + v) * CPW + 16 * j + (lane & 15)] = LR_E(1, i, j)[v];
 #pragma unroll
         for (int q = 0; q < PERL; ++q) {
           const int rr = (lane + 64 * q) / CH;
@@ -713,7 +788,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       for (int q = 0; q < PERL; ++q) {
         const int id = lane + 64 * q;
         const int rr = id / CH;
-        const int lrow = w0m + 16 * i + rr;  // row within the block tile
+        const int lrow = rb + 16 * i + rr;  // row within the block tile
         const int gr = m0 + lrow;
         float v[8];
         {
@@ -738,7 +813,8 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] += rv[e];
           }
-          gstore8<bf16_t>(static_cast<bf16_t*>(g.c[slot]) + (int64_t)gr * g.ldc[slot] + gcl, nvl, v);
+          gstore8<bf16_t>(static_cast<bf16_t*>(pick3(g.c, slot)) + (int64_t)gr * pick3(g.ldc, slot) + gcl,
+                          nvl, v);
         } else if constexpr (EPI == EPI_ORMS) {
           const float sc = sRow[lrow];
 #pragma unroll
@@ -780,12 +856,12 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
         } else if constexpr (EPI == EPI_WGRAD) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] *= gm[e];
-          gstore8<float>(static_cast<float*>(g.c[slot]) + split * g.c_split_stride +
-                             (int64_t)gr * g.ldc[slot] + gcl, nvl, v);
+          gstore8<float>(static_cast<float*>(pick3(g.c, slot)) + split * g.c_split_stride +
+                             (int64_t)gr * pick3(g.ldc, slot) + gcl, nvl, v);
         }
       }
       if constexpr (HAS_RES || HAS_ROW) {
-        if (i + 1 < FM) cur = nxt;
+        if (i + 1 < FME) cur = nxt;
       }
     }
   }
@@ -813,6 +889,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       if (n0 + c < N) g.colsum[(int64_t)tm * N + n0 + c] = s;
     }
   }
+#undef LR_E
 }
 
 }  // namespace lr

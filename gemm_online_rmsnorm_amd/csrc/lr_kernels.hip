@@ -118,6 +118,9 @@ using P128x128 = Tile2<128, 128, 64, 2, 2, 2>;
 using P2x256x128 = Tile2<256, 128, 32, 4, 2, 3>;
 using P2x128x128 = Tile2<128, 128, 32, 2, 2, 3>;
 using P3x128x128 = Tile2<128, 128, 32, 2, 4, 3>;
+// Gate and up products side by side: 256 x (128 gate + 128 up) B rows,
+// 8 waves each running one pair on a 128 x 64 wave tile.
+using PS256x128 = Tile2<256, 256, 32, 2, 4, 3, 2>;
 
 template <class TL, int NPAIR, uint32_t MC, int EPI>
 static hipError_t launch2(const GemmDesc& d, int groups, hipStream_t s) {
@@ -136,7 +139,7 @@ static hipError_t launch2(const GemmDesc& d, int groups, hipStream_t s) {
   g.N = d.N;
   g.K = d.K;
   g.tiles_m = (d.M + TL::BM - 1) / TL::BM;
-  g.tiles_n = (d.N + TL::BN - 1) / TL::BN;
+  g.tiles_n = (d.N + TL::BNO - 1) / TL::BNO;
   for (int i = 0; i < 3; ++i) {
     g.a[i] = d.a[i];
     g.lda[i] = d.lda[i];
@@ -272,12 +275,12 @@ static hipError_t run_gemm2(int op, const GemmDesc& d, int groups, hipStream_t s
     case OP_NN_STORE: return launch_single<EPI_STORE, 2u>(d, groups, s);
     case OP_NN_RMSBWD: return launch_single<EPI_RMSBWD, 2u>(d, groups, s);
     case OP_NT_SWIGLU:
-      if (ntiles(d, 256, 128, 1) >= kCUs) return launch2<P2x256x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
+      if (ntiles(d, 256, 128, 1) >= kCUs) return launch2<PS256x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
       return launch2<P2x128x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
     case OP_SWIGLU_BWD: return launch2<P3x128x128, 3, 32u, EPI_SWIGLU_BWD>(d, 1, s);
     case OP_SWIGLU_BWD2:
       if (ntiles(d, 256, 128, 1) >= kCUs)
-        return launch2<P2x256x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
+        return launch2<PS256x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
       return launch2<P2x128x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
     default: return hipErrorInvalidValue;
   }
