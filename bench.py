@@ -30,6 +30,8 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 MFMA_FP32_PEAK_TFLOPS = 157.3    # MI355X dense fp32
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+COPY_BYTES = 1 << 30             # calibration copy for the byte counters
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
 def _parse():
@@ -42,6 +44,9 @@ def _parse():
                     help="tokens of the workload the CPU oracle runs for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true", help="also print the per-kernel table")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help=f"first make one device copy of {COPY_BYTES} bytes, the reference "
+                         "rocprofv3 byte counters are scaled by")
     return ap.parse_args()
 
 
@@ -97,6 +102,12 @@ def main():
     run = BlockRun(s.T, s.d, s.r, s.F, s.D, s.P, s.dtype, s.eps, s.partials, inputs,
                    heads=s.heads)
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         run.step(stream)
@@ -149,6 +160,15 @@ def main():
         "traffic": None,
         "ms_per_launch": dom["ms"],
     }
+    # Measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE,
+    # copy-calibrated), when taken on the current kernel sources.
+    from gemm_online_rmsnorm_amd import traffic as lrtraffic
+    for name in sorted(os.listdir(TRAFFIC_DIR)) if os.path.isdir(TRAFFIC_DIR) else []:
+        if name.startswith("traffic_") and name.endswith(".json"):
+            rec = lrtraffic.load(os.path.join(TRAFFIC_DIR, name))
+            if rec and rec.get("bench_name") == dom["kernel"]:
+                roofline["traffic"] = rec["traffic_bytes"]
+                roofline["traffic_algorithmic_bytes"] = round(work[dom["kernel"]][1])
     roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
 
     flop_step = s.T * (s.fwd_flop_per_token() + s.bwd_flop_per_token()
