@@ -136,13 +136,17 @@ struct Opnd {
   static_assert(KC || (R >= 128 && 64 % CPK == 0) || (KC), "M-contiguous tiles need R >= 128");
 
   // Consecutive loads of a lane step through rows (KC) or k-rows (MC) by
-  // VROWS, a multiple of the swizzle period, so every load of a lane has
-  // the same chunk swizzle and one per-lane offset serves them all; the
-  // load index moves the base of the buffer resource (KC) or goes into the
-  // scalar offset (MC). This keeps vector registers free for fragments.
+  // VROWS. The chunk swizzle repeats every SWP rows, so loads v and
+  // v + NOFF share their swizzle: NOFF per-lane offsets serve all loads of
+  // a lane, the rest of the load index moving the base of the buffer
+  // resource (KC) or going into the scalar offset (MC). This keeps vector
+  // registers free for fragments.
   static constexpr int VROWS = NWAVE * (KC ? RPB : KPB);
-  uint32_t off;    // per-lane byte offset of load 0 (tile origin, k0 = 0)
-  uint32_t vstep;  // bytes between consecutive loads of a lane
+  static constexpr int SWP = KC ? (BK == 64 ? 16 : 8) : 16;
+  static constexpr int gcd_(int a, int b) { return b ? gcd_(b, a % b) : a; }
+  static constexpr int NOFF = SWP / gcd_(VROWS, SWP) < PER ? SWP / gcd_(VROWS, SWP) : PER;
+  uint32_t off[NOFF];  // per-lane byte offsets of loads 0 .. NOFF-1 (tile origin, k0 = 0)
+  uint32_t vstep;      // bytes between loads v and v + NOFF
 
   // Elements from the operand's first element to one past its last one.
   __device__ static __forceinline__ int64_t extent(int64_t ld, int Rtot, int K) {
@@ -162,25 +166,28 @@ struct Opnd {
   // only feed outputs that are never stored). M-contiguous column chunks
   // past Rtot are clamped to the last one.
   __device__ __forceinline__ void init(int64_t ld, int r0, int Rtot, int lane, int wave) {
-    static_assert(KC ? VROWS % (BK == 64 ? 16 : 8) == 0 : VROWS % 16 == 0,
-                  "loads of a lane must share their swizzle");
+    static_assert((NOFF * VROWS) % SWP == 0 || NOFF == PER, "loads v and v + NOFF must share a swizzle");
     // The same in every lane; kept in a scalar register so the buffer
     // resources built from it are scalar too.
-    vstep = (uint32_t)wave_uniform((int)(2 * (int64_t)VROWS * ld));
-    int64_t e;
-    if constexpr (KC) {
-      const int row = wave * RPB + lane / CPR;
-      const int c = (lane % CPR) ^ swz_kc(row);
-      e = (int64_t)(r0 + row) * ld + 8 * c;
-    } else {
-      const int k = wave * KPB + lane / CPK;
-      const int c = (lane % CPK) ^ swz_mc(k);
-      int gc = r0 / 8 + c;
-      const int last = Rtot / 8 - 1;
-      gc = gc < last ? gc : last;
-      e = (int64_t)k * ld + 8 * gc;
+    vstep = (uint32_t)wave_uniform((int)(2 * (int64_t)NOFF * VROWS * ld));
+#pragma unroll
+    for (int v = 0; v < NOFF; ++v) {
+      const int b = v * NWAVE + wave;
+      int64_t e;
+      if constexpr (KC) {
+        const int row = b * RPB + lane / CPR;
+        const int c = (lane % CPR) ^ swz_kc(row);
+        e = (int64_t)(r0 + row) * ld + 8 * c;
+      } else {
+        const int k = b * KPB + lane / CPK;
+        const int c = (lane % CPK) ^ swz_mc(k);
+        int gc = r0 / 8 + c;
+        const int last = Rtot / 8 - 1;
+        gc = gc < last ? gc : last;
+        e = (int64_t)k * ld + 8 * gc;
+      }
+      off[v] = (uint32_t)(2 * e);
     }
-    off = (uint32_t)(2 * e);
   }
 
   // Issue this stage's loads: `src` points at the tile's k0 (element (r, k0)
@@ -197,18 +204,19 @@ struct Opnd {
 #pragma unroll
     for (int v = 0; v < PER; ++v) {
       const int b = v * NWAVE + wave;
+      const uint32_t vo = off[v % NOFF];
+      const uint32_t step = (uint32_t)(v / NOFF) * vstep;
       if constexpr (KC) {
-        const uint32_t adv = (uint32_t)wave_uniform((int)((uint32_t)v * vstep));
+        const uint32_t adv = (uint32_t)wave_uniform((int)step);
         const int rem = wave_uniform((int)(nbytes > adv ? nbytes - adv : 0u));
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<unsigned char*>(reinterpret_cast<const unsigned char*>(src)) + adv, (short)0,
             rem, 0x00020000);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LR_LPTR(dst + b * 1024), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LR_LPTR(dst + b * 1024), 16, vo, 0, 0, 0);
       } else {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<bf16_t*>(src), (short)0, (int)nbytes, 0x00020000);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LR_LPTR(dst + b * 1024), 16, off, v * vstep, 0,
-                                                 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LR_LPTR(dst + b * 1024), 16, vo, step, 0, 0);
       }
     }
 #else
@@ -308,7 +316,8 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   // so the younger one (waves NWAVE / 2 ..) ends each K-tile alone while
   // the older one waits at the barrier. When every operand is K-contiguous
   // the older waves therefore issue all HBM-to-LDS loads (measured: 7%
-  // faster 256 x 256 tiles); otherwise every wave issues its share.
+  // faster 256 x 256 tiles; no gain measured with M/N-contiguous operands,
+  // which keep every wave issuing its share).
   constexpr int NDMA = (TL::NWAVE == 8 && MCMASK == 0u) ? TL::NWAVE / 2 : TL::NWAVE;
   using OA0 = Opnd<BM, BK, NDMA, !(MCMASK & 1u)>;
   using OB0 = Opnd<BNO, BK, NDMA, !(MCMASK & 2u)>;
