@@ -425,15 +425,17 @@ __device__ __forceinline__ void gload8(const T* p, int n, float* v) {
 
 template <typename T>
 __device__ __forceinline__ void gstore8(T* p, int n, const float* v) {
+  // Outputs are streamed (non-temporal): no later access of this kernel
+  // reads them, and they are far larger than the L2.
   if constexpr (sizeof(T) == 2) {
     if (n >= 8) {
-      *reinterpret_cast<u32x4*>(p) = pack16<T>(v);
+      __builtin_nontemporal_store(pack16<T>(v), reinterpret_cast<u32x4*>(p));
       return;
     }
   } else {
     if (n >= 8) {
-      *reinterpret_cast<u32x4*>(p) = pack16<T>(v);
-      *reinterpret_cast<u32x4*>(p + 4) = pack16<T>(v + 4);
+      __builtin_nontemporal_store(pack16<T>(v), reinterpret_cast<u32x4*>(p));
+      __builtin_nontemporal_store(pack16<T>(v + 4), reinterpret_cast<u32x4*>(p + 4));
       return;
     }
   }

@@ -416,12 +416,27 @@ __global__ __launch_bounds__(256) void rowdot_coef_kernel(const T* __restrict__ 
     const T* pa = a + (int64_t)t * lda;
     const T* pb = b + (int64_t)t * ldb;
     float acc = 0.f;
-    for (int c = lane * VEC; c < width; c += 64 * VEC) {
-      float x[VEC], y[VEC];
-      unpack16<T>(*reinterpret_cast<const u32x4*>(pa + c), x);
-      unpack16<T>(*reinterpret_cast<const u32x4*>(pb + c), y);
+    // Up to U chunks of both rows are in flight before the first FMA.
+    constexpr int U = 8;
+    for (int c0 = lane * VEC; c0 < width; c0 += U * 64 * VEC) {
+      u32x4 ra[U], rb[U];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc = __builtin_fmaf(x[e], y[e], acc);
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * 64 * VEC;
+        ra[u] = rb[u] = u32x4{0u, 0u, 0u, 0u};
+        if (c < width) {
+          ra[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pa + c));
+          rb[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pb + c));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float x[VEC], y[VEC];
+        unpack16<T>(ra[u], x);
+        unpack16<T>(rb[u], y);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc = __builtin_fmaf(x[e], y[e], acc);
+      }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
