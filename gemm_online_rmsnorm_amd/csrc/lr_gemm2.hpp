@@ -24,10 +24,10 @@
 //    are XOR-swizzled by k-row so the four k-rows of a group and the two
 //    groups read together fall on distinct banks.
 //
-// Requirements (checked by the host): K % BK == 0, 16-byte aligned
-// operands, leading dimensions multiples of 8; M/N-contiguous operands
-// have a row count that is a multiple of 8. Rows beyond M or N are
-// clamped to the last row: they only feed outputs that are never stored.
+// Requirements (checked by the host): K % BK == 0, N % 8 == 0, 16-byte
+// aligned operands, leading dimensions multiples of 8; M/N-contiguous
+// operands have a row count that is a multiple of 8. Rows beyond M or N
+// read zeros or the last row: they only feed outputs that are never stored.
 //
 // MFMA: v_mfma_f32_16x16x32_bf16. Lane group g = lane / 16 holds
 // k = 8g .. 8g + 7 of each 32-wide k step in both operands; the accumulator
@@ -98,6 +98,62 @@ __device__ __forceinline__ void interleave() {
   }
   __builtin_amdgcn_sched_group_barrier(0x008, NMF - (NDS + NVM) * per, 0);
 }
+
+// Epilogue input: four bf16 per lane and fragment, from rows [m0, M) of a
+// matrix, through a buffer resource (one per-lane offset, the band in the
+// scalar offset, the fragment column in the instruction offset; rows past
+// M read zeros).
+struct EpiIn {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __amdgpu_buffer_rsrc_t rs;
+#endif
+  uint32_t voff;  // this lane's byte offset (row, 4-column group) of band 0
+  uint32_t band;  // bytes between bands (16 rows)
+  // A null base gives an empty range: every load then returns zeros.
+  __device__ __forceinline__ void init(const bf16_t* base, int64_t ld, int m0, int n0, int M, int N,
+                                       int row, int col) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const bool live = base != nullptr;
+    const bf16_t* p = live ? base + (int64_t)m0 * ld + n0 : base;
+    int64_t bytes = live ? 2 * ((int64_t)(M - m0 - 1) * ld + (N - n0)) : 0;
+    bytes = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(p), (short)0, (int)bytes, 0x00020000);
+#endif
+    voff = (uint32_t)(2 * ((int64_t)row * ld + col));
+    band = (uint32_t)wave_uniform((int)(2 * 16 * ld));
+  }
+  __device__ __forceinline__ u32x2 load(int i, int j) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_raw_buffer_load_b64(rs, voff + 32 * j, i * band, 0);
+#else
+    return u32x2{0u, 0u};
+#endif
+  }
+};
+
+// One fp32 value per row of the block tile (rows past the end, or a null
+// array, read as zero).
+struct EpiRow {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __amdgpu_buffer_rsrc_t rs;
+#endif
+  uint32_t voff;
+  __device__ __forceinline__ void init(const float* base, int m0, int M, int row) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const bool live = base != nullptr && m0 < M;
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(live ? base + m0 : base), (short)0,
+                                           live ? 4 * (M - m0) : 0, 0x00020000);
+#endif
+    voff = (uint32_t)(4 * row);
+  }
+  __device__ __forceinline__ float load(int i) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, i * 64, 0));
+#else
+    return 0.f;
+#endif
+  }
+};
 
 // Element i (0..2, the same in every lane) of a three-entry argument array.
 template <typename T>
@@ -269,9 +325,10 @@ constexpr int stage_bytes() {
   return (TL::NSPLIT == 2 ? 2 * TL::BM + TL::BN : NPAIR * (TL::BM + TL::BN)) * TL::BK * 2;
 }
 
+// Wave-private epilogue staging: one 16-row band of a wave tile in bf16.
 template <class TL>
 constexpr int epi_wave_bytes() {
-  return 16 * (TL::WTN + 4) * 4;
+  return 16 * TL::WTN * 2;
 }
 
 template <class TL, int NPAIR>
@@ -484,7 +541,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) mfma_step<bf16_t>(fa[buf][i], fb[buf][j], acc[p][i][j]);
+      for (int j = 0; j < FN; ++j) mfma_step<bf16_t>(fb[buf][j], fa[buf][i], acc[p][i][j]);
   };
   // K-tile kt has landed in LDS when at most (K-tiles issued after it) x L
   // loads of this lane remain; `after` is that count of K-tiles.
@@ -639,6 +696,11 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   }
 #define LR_E(p, i, j) acc[SPLITN ? 0 : (p)][SPLITN ? (p) * FME + (i) : (i)][j]
 
+  // The MFMA takes the B fragment as its first operand, so fragment (i, j)
+  // of lane l holds row rb + 16 i + (l & 15) of the block tile at the four
+  // consecutive columns cb + 16 j + 4 (l >> 4) + v, v = 0..3.
+  const int fr = lane & 15, fc = 4 * (lane >> 4);
+
   // Elementwise combination of the accumulators.
   if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
@@ -667,242 +729,225 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
         }
   }
 
-  // Wave-private staging: one 16-row band of the wave tile at a time. Each
-  // lane owns PERL chunks of 8 columns per band, always at the same column
-  // offset, so per-column inputs (gamma) are loaded once; the per-row and
-  // per-element inputs of band i + 1 are loaded while band i is written.
-  constexpr int CPW = TL::WTN + 4;
-  float* sW = reinterpret_cast<float*>(lds + wave * epi_wave_bytes<TL>());
-  constexpr int CH = TL::WTN / 8;           // 8-column chunks per band row
-  constexpr int PERL = 16 * CH / 64;        // chunks per lane per band
-  static_assert((16 * CH) % 64 == 0, "band must split over the lanes");
-  static_assert(64 % CH == 0, "a lane's column chunk must not change across its band chunks");
-  constexpr int NOUT = (EPI == EPI_SWIGLU_BWD) ? 3 : 1;
   constexpr bool HAS_RES = (EPI == EPI_STORE || EPI == EPI_RMSBWD || EPI == EPI_SWIGLU_BWD2);
   constexpr bool HAS_H = (EPI == EPI_RMSBWD);
   constexpr bool HAS_GAMMA = (EPI == EPI_RMSBWD || EPI == EPI_WGRAD);
-  constexpr bool HAS_ROW = (EPI == EPI_STORE || EPI == EPI_RMSBWD);
-  const int c8l = (lane % CH) * 8;             // this lane's column chunk in the band
-  const int gcl = n0 + cb + c8l;              // its global column
-  const int nvl = N - gcl;                     // valid columns of the chunk
-  const bool col_ok = gcl < N;
-  float colacc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) colacc[e] = 0.f;
-  float gm[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) gm[e] = 1.0f;
-  if constexpr (HAS_GAMMA) {
-    if (g.colscale && col_ok) gload8<bf16_t>(static_cast<const bf16_t*>(g.colscale) + gcl, nvl, gm);
-  }
   const bf16_t* resp = static_cast<const bf16_t*>(g.res);
   const bf16_t* hp = static_cast<const bf16_t*>(g.hsrc);
-  const float* rowp = (EPI == EPI_RMSBWD) ? g.rowcoef : g.rowdiv;
 
-  // Raw per-band inputs of one lane: PERL chunks of residual / H and a row scalar.
-  struct BandIn {
-    u32x4 r[PERL], h[PERL];
-    float f[PERL];
-  };
-  auto load_band = [&](int i, BandIn& in) {
+  // Band by band, each lane combines its accumulators with the element
+  // inputs (loaded one or two bands ahead), packs the outputs to bf16 and
+  // the wave stages the band through LDS for full-row 16-byte stores. Every
+  // input of a band is requested before the stores of the bands ahead of
+  // it: loads and stores retire through one in-order counter, so a load
+  // issued after a store cannot be waited for without waiting for the store.
+  float gmv[FN][4];  // gamma of this lane's columns
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) gmv[j][v] = 1.0f;
+  if constexpr (HAS_GAMMA) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    // Columns past the end read as zero; no gamma array means gamma = 1.
+    const bool gon = g.colscale != nullptr;
+    const bf16_t* gp = static_cast<const bf16_t*>(g.colscale);
+    const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(gon ? gp + n0 : gp), (short)0, gon ? 2 * (N - n0) : 0, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(grs, 2 * (cb + 16 * j + fc), 0, 0);
+      if (gon) {
+        gmv[j][0] = bf16_lo(w[0]);
+        gmv[j][1] = bf16_hi(w[0]);
+        gmv[j][2] = bf16_lo(w[1]);
+        gmv[j][3] = bf16_hi(w[1]);
+      }
+    }
+#endif
+  }
+
+  // Element inputs in the accumulator layout: 4 bf16 (8 bytes) per fragment.
+  EpiIn in_res, in_h;
+  if constexpr (HAS_RES) in_res.init(resp, g.ldres, m0, n0, M, N, rb + fr, cb + fc);
+  if constexpr (HAS_H) in_h.init(hp, g.ldh, m0, n0, M, N, rb + fr, cb + fc);
+  // Per-row scalars: the RMSNorm-backward coefficient, or the divisor of a
+  // plain store.
+  constexpr bool HAS_ROW = (EPI == EPI_STORE || EPI == EPI_RMSBWD);
+  EpiRow in_row;
+  if constexpr (HAS_ROW) in_row.init(EPI == EPI_RMSBWD ? g.rowcoef : g.rowdiv, m0, M, rb + fr);
+  float colacc[FN][4];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) colacc[j][v] = 0.f;
+
+  // Staging of one band's bf16 outputs: rows of WTN elements, 16-byte chunks
+  // XOR-swizzled so the 8-byte writes (16 rows x 4 lane groups) and the
+  // 16-byte reads (whole rows) both spread over all banks.
+  static_assert(TL::WTN == 64 || TL::WTN == 32, "staging supports 32- and 64-column wave tiles");
+  constexpr int RB = TL::WTN * 2;     // bytes per staged row
+  constexpr int CH = TL::WTN / 8;     // 16-byte chunks per row
+  constexpr int PERL = 16 * CH / 64;  // chunks per lane per band
+  auto swz_st = [](int row) { return RB == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3); };
+  unsigned char* sWb = lds + wave * epi_wave_bytes<TL>();
+  auto put_band = [&](int i, const u32x2 (&w)[FN], void* cbase, int64_t ldc) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int c = 2 * j + (lane >> 5), h = (lane >> 4) & 1;  // logical chunk, 8-byte half
+      *reinterpret_cast<u32x2*>(sWb + fr * RB + 16 * (c ^ swz_st(fr)) + 8 * h) = w[j];
+    }
 #pragma unroll
     for (int q = 0; q < PERL; ++q) {
-      const int rr = (lane + 64 * q) / CH;
-      const int gr = m0 + rb + 16 * i + rr;
-      const bool ok = col_ok && gr < M;
-      in.r[q] = u32x4{0u, 0u, 0u, 0u};
-      in.h[q] = u32x4{0u, 0u, 0u, 0u};
-      in.f[q] = 1.0f;
-      if constexpr (HAS_RES) {
-        if (ok && resp) {  // residual, upstream gradient or dm
-          const bf16_t* src = resp + (int64_t)gr * g.ldres + gcl;
-          if (nvl >= 8) {
-            in.r[q] = *reinterpret_cast<const u32x4*>(src);
-          } else {
-            float t[8];
-            gload8<bf16_t>(src, nvl, t);
-            in.r[q] = pack16<bf16_t>(t);
-          }
-        }
-      }
-      if constexpr (HAS_H) {
-        if (ok) {
-          const bf16_t* src = hp + (int64_t)gr * g.ldh + gcl;
-          if (nvl >= 8) {
-            in.h[q] = *reinterpret_cast<const u32x4*>(src);
-          } else {
-            float t[8];
-            gload8<bf16_t>(src, nvl, t);
-            in.h[q] = pack16<bf16_t>(t);
-          }
-        }
-      }
-      if constexpr (HAS_ROW) {
-        if (ok && rowp) in.f[q] = rowp[gr];
-      }
+      const int id = lane + 64 * q, rr = id / CH, cc = id % CH;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(sWb + rr * RB + 16 * (cc ^ swz_st(rr)));
+      const int gr = m0 + rb + 16 * i + rr, gc = n0 + cb + 8 * cc;
+      if (gr < M && gc < N)
+        __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(static_cast<bf16_t*>(cbase) +
+                                                               (int64_t)gr * ldc + gc));
     }
   };
 
+  constexpr int NOUT = (EPI == EPI_SWIGLU_BWD || EPI == EPI_SWIGLU_BWD2) ? 3 : 1;
+  constexpr int PD = (HAS_H || SPLITN) ? 1 : 2;  // bands of inputs in flight
+  u32x2 rin[FME][FN], hin[FME][FN];
+  float rowv[FME];
+  auto load_band = [&](int i) {
+    if constexpr (HAS_ROW) rowv[i] = in_row.load(i);
 #pragma unroll
-  for (int o = 0; o < NOUT; ++o) {
-    const int ao = (EPI == EPI_SWIGLU_BWD) ? o : 0;
-    BandIn cur, nxt;
-    if constexpr (HAS_RES || HAS_ROW) load_band(0, cur);
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (HAS_RES) rin[i][j] = in_res.load(i, j);
+      if constexpr (HAS_H) hin[i][j] = in_h.load(i, j);
+    }
+  };
+  auto unpack4 = [](u32x2 w, float* x) {
+    x[0] = bf16_lo(w[0]);
+    x[1] = bf16_hi(w[0]);
+    x[2] = bf16_lo(w[1]);
+    x[3] = bf16_hi(w[1]);
+  };
+
+  if constexpr (EPI != EPI_WGRAD) {
+    if constexpr (HAS_RES || HAS_H || HAS_ROW) {
+#pragma unroll
+      for (int i = 0; i < PD && i < FME; ++i) load_band(i);
+    }
 #pragma unroll
     for (int i = 0; i < FME; ++i) {
-      if constexpr (HAS_RES || HAS_ROW) {
-        if (i + 1 < FME) load_band(i + 1, nxt);
+      if constexpr (HAS_RES || HAS_H || HAS_ROW) {
+        if (i + PD < FME) load_band(i + PD);
       }
+      sched_fence();  // keep each band's work together: bounds live registers
+      float rs = 1.0f;  // 1 / rms_g, 1 / rowdiv, or the RMSNorm-backward coefficient
+      if constexpr (ORMS) rs = sRow[rb + 16 * i + fr];
+      if constexpr (EPI == EPI_STORE) rs = 1.0f / rowv[i];
+      if constexpr (EPI == EPI_RMSBWD) rs = rowv[i];
+      u32x2 pk[NOUT][FN];  // this band's packed bf16 outputs
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        float o[NOUT][4];
+        float rv[4] = {0.f, 0.f, 0.f, 0.f}, hv[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (HAS_RES) unpack4(rin[i][j], rv);
+        if constexpr (HAS_H) unpack4(hin[i][j], hv);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float x = LR_E(0, i, j)[v];
+          if constexpr (EPI == EPI_STORE) {
+            o[0][v] = (g.rowdiv ? x * rs : x) + rv[v];
+          } else if constexpr (EPI == EPI_ORMS) {
+            o[0][v] = x * rs;
+          } else if constexpr (EPI == EPI_SWIGLU) {
+            o[0][v] = x;  // already combined
+          } else if constexpr (EPI == EPI_RMSBWD) {
+            // dX = dY + gamma (dZ_n A) - coef H; gamma-gradient sums of acc H
+            colacc[j][v] += x * hv[v];
+            o[0][v] = rv[v] + gmv[j][v] * x - rs * hv[v];
+          } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+            o[0][v] = x;
+            o[1][v] = LR_E(1, i, j)[v];
+            o[2][v] = LR_E(2, i, j)[v];
+          } else if constexpr (EPI == EPI_SWIGLU_BWD2) {
+            // g, u recomputed in the accumulators, dm from HBM:
+            // m = SiLU(g) u; dg = dm u sig(g)(1 + g(1 - sig(g))); du = dm SiLU(g)
+            const float uu = LR_E(1, i, j)[v], dm = rv[v];
+            const float sg = sigmoid_f<bf16_t>(x);
+            const float sl = x * sg;
+            o[0][v] = sl * uu;
+            o[1][v] = dm * uu * sg * (1.0f + x * (1.0f - sg));
+            o[2][v] = dm * sl;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < NOUT; ++q)
+          pk[q][j] = u32x2{pack_bf16x2(o[q][0], o[q][1]), pack_bf16x2(o[q][2], o[q][3])};
+        // Left to itself the compiler sinks the column sums to their use
+        // after the last band and holds the H values of every band until then.
+        if constexpr (HAS_H) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) asm volatile("" : "+v"(colacc[j][v]));
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < NOUT; ++q) {
+        void* cq = (EPI == EPI_STORE) ? pick3(g.c, slot) : pick3(g.c, q);
+        const int64_t lq = (EPI == EPI_STORE) ? pick3(g.ldc, slot) : pick3(g.ldc, q);
+        put_band(i, pk[q], cq, lq);
+      }
+    }
+  }
+
+
+  if constexpr (EPI == EPI_RMSBWD) {
+    // This wave's column sums: the 16 lanes holding the same columns add
+    // theirs (a butterfly over lane bits 0..3); the NWM waves of a column
+    // band are then added through LDS in wave order (fixed order).
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float x = colacc[j][v];
+        x += __shfl_xor(x, 1, 64);
+        x += __shfl_xor(x, 2, 64);
+        x += __shfl_xor(x, 4, 64);
+        x += __shfl_xor(x, 8, 64);
+        colacc[j][v] = x;
+      }
+    float* sCol = reinterpret_cast<float*>(lds + TL::NWAVE * epi_wave_bytes<TL>());  // [NWM][BN]
+    if (fr == 0) {
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          sW[(4 * (lane >> 4) + v) * CPW + 16 * j + (lane & 15)] = LR_E(ao, i, j)[v];
-      // SwiGLU backward from dm: the up accumulator goes through the same
-      // staging area after the gate values have been read out.
-      float ub[PERL][8];
-      if constexpr (EPI == EPI_SWIGLU_BWD2) {
-        float gb[PERL][8];
+        for (int v = 0; v < 4; ++v) sCol[wm * BN + cb + 16 * j + fc + v] = colacc[j][v];
+    }
+  }
+
+  if constexpr (EPI == EPI_WGRAD) {
+    // fp32 weight gradients straight from the accumulators: 16 bytes per
+    // lane, 16 rows x 64 bytes per store.
 #pragma unroll
-        for (int q = 0; q < PERL; ++q) {
-          const int rr = (lane + 64 * q) / CH;
-          const f32x4 x0 = *reinterpret_cast<const f32x4*>(sW + rr * CPW + c8l);
-          const f32x4 x1 = *reinterpret_cast<const f32x4*>(sW + rr * CPW + c8l + 4);
+    for (int i = 0; i < FME; ++i) {
+      const int gr = m0 + rb + 16 * i + fr;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            gb[q][e] = x0[e];
-            gb[q][4 + e] = x1[e];
-          }
+      for (int j = 0; j < FN; ++j) {
+        const int gc = n0 + cb + 16 * j + fc;
+        if (gr < M && gc < N) {
+          const f32x4 x = LR_E(0, i, j);
+          __builtin_nontemporal_store(
+              f32x4{x[0] * gmv[j][0], x[1] * gmv[j][1], x[2] * gmv[j][2], x[3] * gmv[j][3]},
+              reinterpret_cast<f32x4*>(static_cast<float*>(pick3(g.c, slot)) + split * g.c_split_stride +
+                                       (int64_t)gr * pick3(g.ldc, slot) + gc));
         }
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            sW[(4 * (lane >> 4) + v) * CPW + 16 * j + (lane & 15)] = LR_E(1, i, j)[v];
-#pragma unroll
-        for (int q = 0; q < PERL; ++q) {
-          const int rr = (lane + 64 * q) / CH;
-          const f32x4 x0 = *reinterpret_cast<const f32x4*>(sW + rr * CPW + c8l);
-          const f32x4 x1 = *reinterpret_cast<const f32x4*>(sW + rr * CPW + c8l + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            ub[q][e] = x0[e];
-            ub[q][4 + e] = x1[e];
-          }
-        }
-        // gate values back in place of the up values for the common read below
-#pragma unroll
-        for (int q = 0; q < PERL; ++q) {
-          const int rr = (lane + 64 * q) / CH;
-          *reinterpret_cast<f32x4*>(sW + rr * CPW + c8l) =
-              f32x4{gb[q][0], gb[q][1], gb[q][2], gb[q][3]};
-          *reinterpret_cast<f32x4*>(sW + rr * CPW + c8l + 4) =
-              f32x4{gb[q][4], gb[q][5], gb[q][6], gb[q][7]};
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < PERL; ++q) {
-        const int id = lane + 64 * q;
-        const int rr = id / CH;
-        const int lrow = rb + 16 * i + rr;  // row within the block tile
-        const int gr = m0 + lrow;
-        float v[8];
-        {
-          const f32x4 x0 = *reinterpret_cast<const f32x4*>(sW + rr * CPW + c8l);
-          const f32x4 x1 = *reinterpret_cast<const f32x4*>(sW + rr * CPW + c8l + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[e] = x0[e];
-            v[4 + e] = x1[e];
-          }
-        }
-        if (gr >= M || !col_ok) continue;
-        if constexpr (EPI == EPI_STORE) {
-          if (rowp) {
-            const float sc = 1.0f / cur.f[q];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] *= sc;
-          }
-          if (resp) {
-            float rv[8];
-            unpack16<bf16_t>(cur.r[q], rv);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] += rv[e];
-          }
-          gstore8<bf16_t>(static_cast<bf16_t*>(pick3(g.c, slot)) + (int64_t)gr * pick3(g.ldc, slot) + gcl,
-                          nvl, v);
-        } else if constexpr (EPI == EPI_ORMS) {
-          const float sc = sRow[lrow];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] *= sc;
-          gstore8<bf16_t>(static_cast<bf16_t*>(g.c[0]) + (int64_t)gr * g.ldc[0] + gcl, nvl, v);
-        } else if constexpr (EPI == EPI_SWIGLU) {
-          gstore8<bf16_t>(static_cast<bf16_t*>(g.c[0]) + (int64_t)gr * g.ldc[0] + gcl, nvl, v);
-        } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-          gstore8<bf16_t>(static_cast<bf16_t*>(g.c[o]) + (int64_t)gr * g.ldc[o] + gcl, nvl, v);
-        } else if constexpr (EPI == EPI_SWIGLU_BWD2) {
-          // v = g, ub = u, dm from the prefetched band inputs:
-          // m = SiLU(g) u; dg = dm u sig(g)(1 + g(1 - sig(g))); du = dm SiLU(g)
-          float dmv[8], mo[8], dgo[8], duo[8];
-          unpack16<bf16_t>(cur.r[q], dmv);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float gg = v[e], uu = ub[q][e];
-            const float sg = sigmoid_f<bf16_t>(gg);
-            const float sl = gg * sg;
-            mo[e] = sl * uu;
-            dgo[e] = dmv[e] * uu * sg * (1.0f + gg * (1.0f - sg));
-            duo[e] = dmv[e] * sl;
-          }
-          const int64_t off = (int64_t)gr * g.ldc[0] + gcl;
-          gstore8<bf16_t>(static_cast<bf16_t*>(g.c[0]) + off, nvl, mo);
-          gstore8<bf16_t>(static_cast<bf16_t*>(g.c[1]) + (int64_t)gr * g.ldc[1] + gcl, nvl, dgo);
-          gstore8<bf16_t>(static_cast<bf16_t*>(g.c[2]) + (int64_t)gr * g.ldc[2] + gcl, nvl, duo);
-        } else if constexpr (EPI == EPI_RMSBWD) {
-          float hv[8], rv[8];
-          unpack16<bf16_t>(cur.h[q], hv);
-          unpack16<bf16_t>(cur.r[q], rv);
-          const float cf = cur.f[q];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            colacc[e] += v[e] * hv[e];
-            v[e] = rv[e] + gm[e] * v[e] - cf * hv[e];
-          }
-          gstore8<bf16_t>(static_cast<bf16_t*>(g.c[0]) + (int64_t)gr * g.ldc[0] + gcl, nvl, v);
-        } else if constexpr (EPI == EPI_WGRAD) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] *= gm[e];
-          gstore8<float>(static_cast<float*>(pick3(g.c, slot)) + split * g.c_split_stride +
-                             (int64_t)gr * pick3(g.ldc, slot) + gcl, nvl, v);
-        }
-      }
-      if constexpr (HAS_RES || HAS_ROW) {
-        if (i + 1 < FME) cur = nxt;
       }
     }
   }
 
   if constexpr (EPI == EPI_RMSBWD) {
-    // Column sums of acc * H over this tile's rows, in a fixed order:
-    // lanes sharing columns (lane % CH) first, then the NWM waves of a column
-    // band through LDS.
-    static_assert(64 % CH == 0, "lanes must tile the band's chunks");
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-#pragma unroll
-      for (int off = CH; off < 64; off <<= 1) colacc[e] += __shfl_xor(colacc[e], off, 64);
-    }
-    float* sCol = reinterpret_cast<float*>(lds + TL::NWAVE * epi_wave_bytes<TL>());  // [NWM][BN]
-    if (lane < CH) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sCol[wm * BN + w0n + lane * 8 + e] = colacc[e];
-    }
+    const float* sCol = reinterpret_cast<const float*>(lds + TL::NWAVE * epi_wave_bytes<TL>());
     __syncthreads();
     for (int c = tid; c < BN; c += TL::NT) {
-      float s = 0.f;
+      float sum = 0.f;
 #pragma unroll
-      for (int q = 0; q < TL::NWM; ++q) s += sCol[q * BN + c];
-      if (n0 + c < N) g.colsum[(int64_t)tm * N + n0 + c] = s;
+      for (int q = 0; q < TL::NWM; ++q) sum += sCol[q * BN + c];
+      if (n0 + c < N) g.colsum[(int64_t)tm * N + n0 + c] = sum;
     }
   }
 #undef LR_E

@@ -186,7 +186,7 @@ static int64_t operand_extent(bool mc, int64_t ld, int rows, int K) {
 }
 
 static bool eligible2(int op, const GemmDesc& d, int groups, int bk) {
-  if (d.K % bk != 0 || d.M < 1 || d.N < 1) return false;
+  if (d.K % bk != 0 || d.M < 1 || d.N < 1 || d.N % 8 != 0) return false;
   uint32_t mc = 0;
   int npair = 1;
   switch (op) {
