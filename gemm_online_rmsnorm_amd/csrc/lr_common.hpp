@@ -90,15 +90,17 @@ __device__ __forceinline__ u32x4 pack16<float>(const float* in) {
   return v;
 }
 
-// Logistic sigmoid. The bf16 path uses the hardware exp2 approximation (a
-// relative error near 1e-6, far below bf16 rounding); the fp32 path uses the
-// accurate library exp and a true division.
+// Logistic sigmoid. The bf16 path uses the hardware exp2 and reciprocal
+// approximations (v_exp_f32, v_rcp_f32: relative errors near 1e-6 and one
+// ulp, far below bf16 rounding; a correctly rounded reciprocal costs ten
+// instructions where v_rcp_f32 costs one); the fp32 path uses the accurate
+// library exp and a true division. exp(-z) = inf gives 0, as it should.
 template <typename T>
 __device__ __forceinline__ float sigmoid_f(float z);
 
 template <>
 __device__ __forceinline__ float sigmoid_f<bf16_t>(float z) {
-  return __frcp_rn(1.0f + __expf(-z));
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
 template <>

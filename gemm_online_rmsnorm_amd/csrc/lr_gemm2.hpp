@@ -99,34 +99,96 @@ __device__ __forceinline__ void interleave() {
   __builtin_amdgcn_sched_group_barrier(0x008, NMF - (NDS + NVM) * per, 0);
 }
 
-// Epilogue input: four bf16 per lane and fragment, from rows [m0, M) of a
-// matrix, through a buffer resource (one per-lane offset, the band in the
-// scalar offset, the fragment column in the instruction offset; rows past
-// M read zeros).
-struct EpiIn {
+// Wait until at most n vector-memory operations of this wave are pending;
+// n is a compile-time constant once the caller's loop is unrolled, and the
+// switch folds to one wait. Counts above 24 wait for 24 (more than needed).
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    case 15: wait_vmcnt<15>(); break;
+    case 16: wait_vmcnt<16>(); break;
+    case 17: wait_vmcnt<17>(); break;
+    case 18: wait_vmcnt<18>(); break;
+    case 19: wait_vmcnt<19>(); break;
+    case 20: wait_vmcnt<20>(); break;
+    case 21: wait_vmcnt<21>(); break;
+    case 22: wait_vmcnt<22>(); break;
+    case 23: wait_vmcnt<23>(); break;
+    default: wait_vmcnt<24>(); break;
+  }
+}
+
+// Epilogue bands. A band is 16 rows of a wave tile; with 64 columns it is
+// held in LDS as 16 rows of 128 bytes whose 16-byte chunks are XOR-swizzled
+// by row, so that the 8-byte accesses of the accumulator layout (lane l:
+// row l & 15, columns 16 j + 4 (l >> 4) .. + 3) and the 16-byte accesses of
+// whole rows both spread over the banks.
+__device__ __forceinline__ int epi_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ uint32_t epi_acc_off(int j, int lane) {
+  const int r = lane & 15, c = 2 * j + (lane >> 5), h = (lane >> 4) & 1;
+  return (uint32_t)(r * 128 + 16 * (c ^ epi_swz(r)) + 8 * h);
+}
+
+// Buffer resource over rows [m0, M) x columns [n0, N) of a row-major bf16 or
+// fp32 matrix (the range ends at its last element; empty for a null base).
+// The range check applies to the per-lane offset only, so every access puts
+// its whole offset there.
+__device__ __forceinline__ void epi_range(const void* base, int esz, int64_t ld, int m0, int n0,
+                                          int M, int N, const unsigned char*& p, int& bytes) {
+  const bool live = base != nullptr && m0 < M && n0 < N;
+  p = static_cast<const unsigned char*>(base) + (live ? esz * ((int64_t)m0 * ld + n0) : 0);
+  int64_t nb = live ? esz * ((int64_t)(M - m0 - 1) * ld + (N - n0)) : 0;
+  bytes = (int)(nb > 0x7FFFFFFF ? 0x7FFFFFFF : nb);
+}
+
+// One bf16 input of the epilogue (residual, upstream gradient, H, dm). A
+// band (16 x 64) is copied by two 1 KB HBM-to-LDS loads, each covering 8
+// whole 128-byte rows, into a wave-private LDS slot in the band layout.
+// Rows past M, and columns past N in the last row, read as zeros; columns
+// past N elsewhere read the next row and are never stored.
+struct EpiDma {
 #if defined(__HIP_DEVICE_COMPILE__)
   __amdgpu_buffer_rsrc_t rs;
 #endif
-  uint32_t voff;  // this lane's byte offset (row, 4-column group) of band 0
-  uint32_t band;  // bytes between bands (16 rows)
-  // A null base gives an empty range: every load then returns zeros.
+  uint32_t voff[2];  // this lane's byte offsets of the two halves of band 0
+  uint32_t band;     // bytes between bands
   __device__ __forceinline__ void init(const bf16_t* base, int64_t ld, int m0, int n0, int M, int N,
-                                       int row, int col) {
+                                       int row0, int col0, int lane) {
+    const unsigned char* p;
+    int bytes;
+    epi_range(base, 2, ld, m0, n0, M, N, p, bytes);
 #if defined(__HIP_DEVICE_COMPILE__)
-    const bool live = base != nullptr;
-    const bf16_t* p = live ? base + (int64_t)m0 * ld + n0 : base;
-    int64_t bytes = live ? 2 * ((int64_t)(M - m0 - 1) * ld + (N - n0)) : 0;
-    bytes = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
-    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(p), (short)0, (int)bytes, 0x00020000);
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(p), (short)0, bytes, 0x00020000);
 #endif
-    voff = (uint32_t)(2 * ((int64_t)row * ld + col));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * h + lane / 8, c = (lane & 7) ^ epi_swz(r);
+      voff[h] = (uint32_t)(2 * ((int64_t)(row0 + r) * ld + col0 + 8 * c));
+    }
     band = (uint32_t)wave_uniform((int)(2 * 16 * ld));
   }
-  __device__ __forceinline__ u32x2 load(int i, int j) const {
+  // Band i into the 2 KB slot `dst` (the same in every lane).
+  __device__ __forceinline__ void issue(int i, unsigned char* dst) const {
 #if defined(__HIP_DEVICE_COMPILE__)
-    return __builtin_amdgcn_raw_buffer_load_b64(rs, voff + 32 * j, i * band, 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LR_LPTR(dst + 1024 * h), 16, voff[h] + i * band, 0, 0, 0);
 #else
-    return u32x2{0u, 0u};
+    (void)i; (void)dst;
 #endif
   }
 };
@@ -139,18 +201,55 @@ struct EpiRow {
 #endif
   uint32_t voff;
   __device__ __forceinline__ void init(const float* base, int m0, int M, int row) {
+    const unsigned char* p;
+    int bytes;
+    epi_range(base, 4, 1, m0, 0, M, 1, p, bytes);
 #if defined(__HIP_DEVICE_COMPILE__)
-    const bool live = base != nullptr && m0 < M;
-    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(live ? base + m0 : base), (short)0,
-                                           live ? 4 * (M - m0) : 0, 0x00020000);
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(p), (short)0, bytes, 0x00020000);
 #endif
     voff = (uint32_t)(4 * row);
   }
   __device__ __forceinline__ float load(int i) const {
 #if defined(__HIP_DEVICE_COMPILE__)
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, i * 64, 0));
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 64 * i, 0, 0));
 #else
     return 0.f;
+#endif
+  }
+};
+
+// Stores of one bf16 output, band by band: 16-byte buffer stores of whole
+// staged rows with the non-temporal hint. Lanes whose chunk starts past the
+// last column get an offset outside the range and rows past the end fall
+// outside it, so every lane issues the same stores.
+template <int PERL>
+struct EpiOut {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __amdgpu_buffer_rsrc_t rs;
+#endif
+  uint32_t voff[PERL];
+  uint32_t band;
+  __device__ __forceinline__ void init(void* base, int64_t ld, int m0, int n0, int M, int N, int row0,
+                                       int col0, int lane, int CH) {
+    const unsigned char* p;
+    int bytes;
+    epi_range(base, 2, ld, m0, n0, M, N, p, bytes);
+#if defined(__HIP_DEVICE_COMPILE__)
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(p), (short)0, bytes, 0x00020000);
+#endif
+#pragma unroll
+    for (int q = 0; q < PERL; ++q) {
+      const int id = lane + 64 * q, rr = id / CH, cc = id % CH;
+      const bool ok = n0 + col0 + 8 * cc < N;
+      voff[q] = ok ? (uint32_t)(2 * ((int64_t)(row0 + rr) * ld + col0 + 8 * cc)) : 0x80000000u;
+    }
+    band = (uint32_t)wave_uniform((int)(2 * 16 * ld));
+  }
+  __device__ __forceinline__ void store(int i, int q, u32x4 x) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_buffer_store_b128(x, rs, voff[q] + i * band, 0, 2 /* nt */);
+#else
+    (void)i; (void)q; (void)x;
 #endif
   }
 };
@@ -331,11 +430,50 @@ constexpr int epi_wave_bytes() {
   return 16 * TL::WTN * 2;
 }
 
-template <class TL, int NPAIR>
-constexpr int gemm2_lds_bytes() {
+// Staging bands (one per wave) and the column sums of the RMSNorm backward.
+template <class TL>
+constexpr int epi_area_bytes() {
+  return TL::NWAVE * epi_wave_bytes<TL>() + TL::NWM * TL::BN * 4;
+}
+template <int EPI>
+constexpr int epi_nin() {
+  return ((EPI == EPI_STORE || EPI == EPI_RMSBWD || EPI == EPI_SWIGLU_BWD2) ? 1 : 0) +
+         (EPI == EPI_RMSBWD ? 1 : 0);
+}
+// Split tiles hand half of their accumulators over through LDS: in one
+// round, or in two rounds of a quarter each when band-input slots must fit
+// beside the exchange area.
+template <int EPI>
+constexpr int epi_xch_rounds() {
+  return epi_nin<EPI>() > 0 ? 2 : 1;
+}
+template <class TL, int EPI>
+constexpr int epi_xch_bytes() {
+  return TL::NSPLIT == 2 ? TL::NWAVE * (TL::FM / 2 / epi_xch_rounds<EPI>()) * TL::FN * 4 * 64 * 4 : 0;
+}
+// First byte of the band-input slots (1 KB aligned, after both areas above).
+template <class TL, int EPI>
+constexpr int epi_in0() {
+  constexpr int a = epi_area_bytes<TL>() > epi_xch_bytes<TL, EPI>() ? epi_area_bytes<TL>()
+                                                                     : epi_xch_bytes<TL, EPI>();
+  return (a + 1023) / 1024 * 1024;
+}
+template <class TL, int EPI>
+constexpr int epi_pds() {
+  constexpr int fme = TL::NSPLIT == 2 ? TL::FM / 2 : TL::FM;
+  constexpr int want = epi_nin<EPI>() == 2 ? 3 : 4;
+  return want < fme ? want : fme;
+}
+template <class TL, int NPAIR, int EPI>
+constexpr int gemm2_body_bytes() {
   constexpr int ring = TL::NSTAGE * stage_bytes<TL, NPAIR>();
-  constexpr int epi = TL::NWAVE * epi_wave_bytes<TL>() + 2 * TL::BN * 8 * 4;
-  return (ring > epi ? ring : epi) + 8 * TL::BM * 4 /* sums of squares */ + TL::BM * 4;
+  constexpr int in_end = epi_in0<TL, EPI>() + TL::NWAVE * epi_pds<TL, EPI>() * epi_nin<EPI>() * 2048;
+  constexpr int epi = in_end > epi_area_bytes<TL>() ? in_end : epi_area_bytes<TL>();
+  return ring > epi ? ring : epi;
+}
+template <class TL, int NPAIR, int EPI>
+constexpr int gemm2_lds_bytes() {
+  return gemm2_body_bytes<TL, NPAIR, EPI>() + 8 * TL::BM * 4 /* sums of squares */ + TL::BM * 4;
 }
 
 // ---------------------------------------------------------------------------
@@ -353,8 +491,12 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   constexpr int SB = stage_bytes<TL, NPAIR>();
   extern __shared__ __align__(16) unsigned char lds[];
   constexpr int RING = S * SB;
-  constexpr int EPIB = TL::NWAVE * epi_wave_bytes<TL>() + 2 * BN * 8 * 4;
-  constexpr int BODY = RING > EPIB ? RING : EPIB;
+  // Epilogue areas (the ring is free by then): staging bands and column
+  // sums, the split-tile exchange, the band-input slots.
+  constexpr int EPIB = epi_area_bytes<TL>();
+  constexpr int XCH = epi_xch_bytes<TL, EPI>();
+  constexpr int IN0 = epi_in0<TL, EPI>();
+  constexpr int BODY = gemm2_body_bytes<TL, NPAIR, EPI>();
   float* sSS = reinterpret_cast<float*>(lds + BODY);  // [8][BM]
   float* sRow = sSS + 8 * BM;                          // [BM]
 
@@ -481,6 +623,10 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   // Per-lane fragment offsets (k-step 0; step 1 adds a constant).
   const int w0m = wm * TL::WTM, w0n = wn * TL::WTN;
   const int pw = SPLITN ? wn / (TL::NWN / 2) : 0;  // the pair a split-tile wave runs
+  // Byte shift of FM/2 row bands in an A stage tile (the swizzle pattern
+  // repeats every 16 rows, so shifted offsets stay valid).
+  const int srot = SPLITN ? pw * (FM / 2) * 16 * BK * 2 : 0;
+  static_assert(!SPLITN || FM % 2 == 0, "split tiles hand over half of the row bands");
 
   // Online RMSNorm: the waves of one row band (same wm) read the same A
   // fragments; wave wn sums the squares of fragments i = wn, wn + NWN, ...
@@ -505,12 +651,16 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     const bool bmc = (MCMASK >> (2 * p + 1)) & 1u;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      // Split tiles: the up-pair waves hold row bands in rotated order
+      // (slot i holds band (i + FM/2) mod FM), so that every wave keeps
+      // slots 0 .. FM/2 - 1 and hands over the rest.
+      const unsigned char* tAi = SPLITN ? (i < FM / 2 ? tA + srot : tA - srot) : tA;
       if (amc)
         fa[buf][i] = Opnd<BM, BK, TL::NWAVE, false>::read_frag(
-            tA, Opnd<BM, BK, TL::NWAVE, false>::frag_off(w0m + 16 * i, s, lane));
+            tAi, Opnd<BM, BK, TL::NWAVE, false>::frag_off(w0m + 16 * i, s, lane));
       else
         fa[buf][i] = Opnd<BM, BK, TL::NWAVE, true>::read_frag(
-            tA, Opnd<BM, BK, TL::NWAVE, true>::frag_off(w0m + 16 * i, s, lane));
+            tAi, Opnd<BM, BK, TL::NWAVE, true>::frag_off(w0m + 16 * i, s, lane));
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -638,6 +788,97 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   sched_fence();
   __syncthreads();  // every wave is done with the ring; sSS is visible
 
+  // Epilogue geometry. Split tiles: the wave running pair 0 (gate) and its
+  // partner in the same row band running pair 1 (up) each finish half of the
+  // bands, handing the other half of their accumulators over through LDS;
+  // afterwards acc[0][i] holds the gate and acc[0][FME + i] the up values of
+  // band keep0 + i. LR_E(p, i, j) names pair p of epilogue band i. Band i
+  // covers rows rb + 16 i .. + 15 and columns cb .. cb + WTN - 1 of the tile.
+  constexpr int FME = SPLITN ? FM / 2 : FM;
+  const int keep0 = pw * FME;
+  const int rb = w0m + 16 * keep0;                                  // first row
+  const int cb = SPLITN ? (wn % (TL::NWN / 2)) * TL::WTN : w0n;  // first column
+  // The MFMA takes the B fragment as its first operand, so fragment (i, j)
+  // of lane l holds row rb + 16 i + (l & 15) of the block tile at the four
+  // consecutive columns cb + 16 j + 4 (l >> 4) + v, v = 0..3.
+  // (The lane index is recomputed here so that the compiler does not keep
+  // values derived from it alive across the main loop.)
+  const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int fr = elane & 15, fc = 4 * (elane >> 4);
+
+  // HBM inputs of the epilogue, requested before anything else: gamma and
+  // the row scalars into registers, the bf16 element inputs (NIN of them)
+  // band by band into wave-private LDS slots, PDS bands ahead.
+  constexpr bool HAS_RES = (EPI == EPI_STORE || EPI == EPI_RMSBWD || EPI == EPI_SWIGLU_BWD2);
+  constexpr bool HAS_H = (EPI == EPI_RMSBWD);
+  constexpr bool HAS_GAMMA = (EPI == EPI_RMSBWD || EPI == EPI_WGRAD);
+  constexpr bool HAS_ROW = (EPI == EPI_STORE || EPI == EPI_RMSBWD);
+  constexpr int NIN = (HAS_RES ? 1 : 0) + (HAS_H ? 1 : 0);
+  constexpr int PDS = epi_pds<TL, EPI>();
+  static_assert(NIN == epi_nin<EPI>(), "input count");
+  static_assert(NIN == 0 || TL::WTN == 64, "band inputs need 64-column wave tiles");
+  static_assert(NIN == 0 || IN0 + TL::NWAVE * PDS * NIN * 2048 <= BODY, "input slots exceed LDS");
+  const bf16_t* resp = static_cast<const bf16_t*>(g.res);
+  const bf16_t* hp = static_cast<const bf16_t*>(g.hsrc);
+
+  float gmv[FN][4];  // gamma of this lane's columns
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) gmv[j][v] = 1.0f;
+  if constexpr (HAS_GAMMA) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    // Columns past the end read as zero; no gamma array means gamma = 1.
+    const bool gon = g.colscale != nullptr;
+    const unsigned char* gp;
+    int gbytes;
+    epi_range(g.colscale, 2, 0, 0, n0, 1, N, gp, gbytes);
+    const __amdgpu_buffer_rsrc_t grs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(gp), (short)0, gbytes, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      // Without a gamma array the load reads zeros and the 1 comes from
+      // `one`: no branch, so the loads need not be waited for here.
+      const float one = gon ? 0.0f : 1.0f;
+      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(grs, 2 * (cb + 16 * j + fc), 0, 0);
+      gmv[j][0] = bf16_lo(w[0]) + one;
+      gmv[j][1] = bf16_hi(w[0]) + one;
+      gmv[j][2] = bf16_lo(w[1]) + one;
+      gmv[j][3] = bf16_hi(w[1]) + one;
+    }
+#endif
+  }
+  // Per-row scalars: the RMSNorm-backward coefficient, or the divisor of a
+  // plain store (rows past the end read zero; they are never stored).
+  float rowv[FME];
+  if constexpr (HAS_ROW) {
+    EpiRow in_row;
+    in_row.init(EPI == EPI_RMSBWD ? g.rowcoef : g.rowdiv, m0, M, rb + fr);
+#pragma unroll
+    for (int i = 0; i < FME; ++i) rowv[i] = in_row.load(i);
+  }
+  // The band inputs' loads are counted by hand below: no other HBM access
+  // may be issued after them but the epilogue's stores.
+  asm volatile("" ::: "memory");
+  sched_fence();
+  EpiDma in_res, in_h;
+  if constexpr (HAS_RES) in_res.init(resp, g.ldres, m0, n0, M, N, rb, cb, lane);
+  if constexpr (HAS_H) in_h.init(hp, g.ldh, m0, n0, M, N, rb, cb, lane);
+  unsigned char* sIn = lds + IN0 + wave * (PDS * NIN * 2048);  // [PDS][NIN][2 KB]
+  // A plain store without a residual has no band inputs.
+  const bool in_on = NIN > 0 && (EPI != EPI_STORE || resp != nullptr);
+  auto issue_band = [&](int i) {
+    unsigned char* slot = sIn + (i % PDS) * (NIN * 2048);
+    if constexpr (HAS_RES) in_res.issue(i, slot);
+    if constexpr (HAS_H) in_h.issue(i, slot + 2048);
+  };
+  if constexpr (NIN > 0) {
+    if (in_on) {
+#pragma unroll
+      for (int i = 0; i < PDS; ++i) issue_band(i);
+    }
+  }
+
   if constexpr (ORMS) {
     for (int r = tid; r < BM; r += TL::NT) {
       float ss = 0.f;
@@ -659,47 +900,46 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  // Split tiles: the wave running pair 0 (gate) and its partner in the same
-  // row band running pair 1 (up) each finish half of the bands, handing the
-  // other half of their accumulators over through LDS (the ring is free).
-  // Afterwards acc[0][i] holds the gate and acc[0][FME + i] the up values of
-  // band keep0 + i. LR_E(p, i, j) names pair p of epilogue band i.
-  constexpr int FME = SPLITN ? FM / 2 : FM;
-  const int keep0 = pw * FME;
-  const int rb = w0m + 16 * keep0;                                  // first row
-  const int cb = SPLITN ? (wn % (TL::NWN / 2)) * TL::WTN : w0n;  // first column
   if constexpr (SPLITN) {
+    constexpr int NRD = epi_xch_rounds<EPI>();
+    static_assert(XCH <= IN0, "the exchange area overlaps the input slots");
+    static_assert(FME % NRD == 0, "exchange rounds split the bands");
+    static_assert(XCH <= RING, "exchange area exceeds the ring");
+    constexpr int NR = FME / NRD;
     const int partner = wm * TL::NWN + (wn + TL::NWN / 2) % TL::NWN;
-    float* xch = reinterpret_cast<float*>(lds);  // [NWAVE][FME][FN][4][64]
-    static_assert(TL::NWAVE * FME * FN * 4 * 64 * 4 <= RING, "exchange area exceeds the ring");
+    float* xch = reinterpret_cast<float*>(lds);  // [NWAVE][NR][FN][4][64]
 #pragma unroll
-    for (int i = 0; i < FME; ++i)
+    for (int rd = 0; rd < NRD; ++rd) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int ii = 0; ii < NR; ++ii)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          xch[(((wave * FME + i) * FN + j) * 4 + v) * 64 + lane] =
-              pw ? acc[0][i][j][v] : acc[0][FME + i][j][v];
-    __syncthreads();
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-    for (int i = 0; i < FME; ++i)
+          for (int v = 0; v < 4; ++v)
+            xch[(((wave * NR + ii) * FN + j) * 4 + v) * 64 + lane] = acc[0][FME + rd * NR + ii][j][v];
+      // A bare barrier: __syncthreads would also wait for the band-input
+      // loads in flight.
+      wait_lgkmcnt0();
+      block_barrier();
+      // Slot i: own pair, band keep0 + i; slot FME + i: the partner's pair,
+      // same band. Put the gate in slot i and the up values in slot FME + i.
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int ii = 0; ii < NR; ++ii)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float other = xch[(((partner * FME + i) * FN + j) * 4 + v) * 64 + lane];
-          const float own = pw ? acc[0][FME + i][j][v] : acc[0][i][j][v];
-          acc[0][i][j][v] = pw ? other : own;
-          acc[0][FME + i][j][v] = pw ? own : other;
-        }
-    __syncthreads();  // the staging area below overlaps the exchange area
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int i = rd * NR + ii;
+            const float own = acc[0][i][j][v];
+            const float oth = xch[(((partner * NR + ii) * FN + j) * 4 + v) * 64 + lane];
+            acc[0][i][j][v] = pw ? oth : own;
+            acc[0][FME + i][j][v] = pw ? own : oth;
+          }
+      wait_lgkmcnt0();
+      block_barrier();  // the next round and the staging area reuse the exchange area
+    }
   }
 #define LR_E(p, i, j) acc[SPLITN ? 0 : (p)][SPLITN ? (p) * FME + (i) : (i)][j]
-
-  // The MFMA takes the B fragment as its first operand, so fragment (i, j)
-  // of lane l holds row rb + 16 i + (l & 15) of the block tile at the four
-  // consecutive columns cb + 16 j + 4 (l >> 4) + v, v = 0..3.
-  const int fr = lane & 15, fc = 4 * (lane >> 4);
 
   // Elementwise combination of the accumulators.
   if constexpr (EPI == EPI_SWIGLU) {
@@ -729,68 +969,29 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
         }
   }
 
-  constexpr bool HAS_RES = (EPI == EPI_STORE || EPI == EPI_RMSBWD || EPI == EPI_SWIGLU_BWD2);
-  constexpr bool HAS_H = (EPI == EPI_RMSBWD);
-  constexpr bool HAS_GAMMA = (EPI == EPI_RMSBWD || EPI == EPI_WGRAD);
-  const bf16_t* resp = static_cast<const bf16_t*>(g.res);
-  const bf16_t* hp = static_cast<const bf16_t*>(g.hsrc);
-
-  // Band by band, each lane combines its accumulators with the element
-  // inputs (loaded one or two bands ahead), packs the outputs to bf16 and
-  // the wave stages the band through LDS for full-row 16-byte stores. Every
-  // input of a band is requested before the stores of the bands ahead of
-  // it: loads and stores retire through one in-order counter, so a load
-  // issued after a store cannot be waited for without waiting for the store.
-  float gmv[FN][4];  // gamma of this lane's columns
-#pragma unroll
-  for (int j = 0; j < FN; ++j)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) gmv[j][v] = 1.0f;
-  if constexpr (HAS_GAMMA) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    // Columns past the end read as zero; no gamma array means gamma = 1.
-    const bool gon = g.colscale != nullptr;
-    const bf16_t* gp = static_cast<const bf16_t*>(g.colscale);
-    const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t*>(gon ? gp + n0 : gp), (short)0, gon ? 2 * (N - n0) : 0, 0x00020000);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(grs, 2 * (cb + 16 * j + fc), 0, 0);
-      if (gon) {
-        gmv[j][0] = bf16_lo(w[0]);
-        gmv[j][1] = bf16_hi(w[0]);
-        gmv[j][2] = bf16_lo(w[1]);
-        gmv[j][3] = bf16_hi(w[1]);
-      }
-    }
-#endif
-  }
-
-  // Element inputs in the accumulator layout: 4 bf16 (8 bytes) per fragment.
-  EpiIn in_res, in_h;
-  if constexpr (HAS_RES) in_res.init(resp, g.ldres, m0, n0, M, N, rb + fr, cb + fc);
-  if constexpr (HAS_H) in_h.init(hp, g.ldh, m0, n0, M, N, rb + fr, cb + fc);
-  // Per-row scalars: the RMSNorm-backward coefficient, or the divisor of a
-  // plain store.
-  constexpr bool HAS_ROW = (EPI == EPI_STORE || EPI == EPI_RMSBWD);
-  EpiRow in_row;
-  if constexpr (HAS_ROW) in_row.init(EPI == EPI_RMSBWD ? g.rowcoef : g.rowdiv, m0, M, rb + fr);
-  float colacc[FN][4];
-#pragma unroll
-  for (int j = 0; j < FN; ++j)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) colacc[j][v] = 0.f;
-
-  // Staging of one band's bf16 outputs: rows of WTN elements, 16-byte chunks
-  // XOR-swizzled so the 8-byte writes (16 rows x 4 lane groups) and the
-  // 16-byte reads (whole rows) both spread over all banks.
+  // Staging of one band's bf16 outputs for whole-row stores.
   static_assert(TL::WTN == 64 || TL::WTN == 32, "staging supports 32- and 64-column wave tiles");
   constexpr int RB = TL::WTN * 2;     // bytes per staged row
   constexpr int CH = TL::WTN / 8;     // 16-byte chunks per row
   constexpr int PERL = 16 * CH / 64;  // chunks per lane per band
-  auto swz_st = [](int row) { return RB == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3); };
+  auto swz_st = [](int row) { return RB == 128 ? epi_swz(row) : ((row >> 2) & 3); };
   unsigned char* sWb = lds + wave * epi_wave_bytes<TL>();
-  auto put_band = [&](int i, const u32x2 (&w)[FN], void* cbase, int64_t ldc) {
+  constexpr int NOUT = (EPI == EPI_SWIGLU_BWD || EPI == EPI_SWIGLU_BWD2) ? 3 : 1;
+  void* cq[NOUT];
+  int64_t lq[NOUT];
+  EpiOut<PERL> outs[NOUT];
+#pragma unroll
+  for (int q = 0; q < NOUT; ++q) {
+    cq[q] = (EPI == EPI_STORE) ? pick3(g.c, slot) : pick3(g.c, q);
+    lq[q] = (EPI == EPI_STORE) ? pick3(g.ldc, slot) : pick3(g.ldc, q);
+    if constexpr (NIN > 0) outs[q].init(cq[q], lq[q], m0, n0, M, N, rb, cb, lane, CH);
+  }
+  // With band inputs in flight every lane must issue the same stores (the
+  // waits count them), so they go through the buffer range check; without,
+  // plain stores of the lanes in range.
+  auto put_band = [&](int i, const u32x2 (&w)[FN], const EpiOut<PERL>& out, void* cbase, int64_t ldc,
+                      auto uniform_tag) {
+    constexpr bool UNIFORM = decltype(uniform_tag)::value;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int c = 2 * j + (lane >> 5), h = (lane >> 4) & 1;  // logical chunk, 8-byte half
@@ -800,23 +1001,14 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     for (int q = 0; q < PERL; ++q) {
       const int id = lane + 64 * q, rr = id / CH, cc = id % CH;
       const u32x4 x = *reinterpret_cast<const u32x4*>(sWb + rr * RB + 16 * (cc ^ swz_st(rr)));
-      const int gr = m0 + rb + 16 * i + rr, gc = n0 + cb + 8 * cc;
-      if (gr < M && gc < N)
-        __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(static_cast<bf16_t*>(cbase) +
-                                                               (int64_t)gr * ldc + gc));
-    }
-  };
-
-  constexpr int NOUT = (EPI == EPI_SWIGLU_BWD || EPI == EPI_SWIGLU_BWD2) ? 3 : 1;
-  constexpr int PD = (HAS_H || SPLITN) ? 1 : 2;  // bands of inputs in flight
-  u32x2 rin[FME][FN], hin[FME][FN];
-  float rowv[FME];
-  auto load_band = [&](int i) {
-    if constexpr (HAS_ROW) rowv[i] = in_row.load(i);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      if constexpr (HAS_RES) rin[i][j] = in_res.load(i, j);
-      if constexpr (HAS_H) hin[i][j] = in_h.load(i, j);
+      if constexpr (UNIFORM) {
+        out.store(i, q, x);
+      } else {
+        const int gr = m0 + rb + 16 * i + rr, gc = n0 + cb + 8 * cc;
+        if (gr < M && gc < N)
+          __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(static_cast<bf16_t*>(cbase) +
+                                                                 (int64_t)gr * ldc + gc));
+      }
     }
   };
   auto unpack4 = [](u32x2 w, float* x) {
@@ -825,18 +1017,50 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     x[2] = bf16_lo(w[1]);
     x[3] = bf16_hi(w[1]);
   };
-
-  if constexpr (EPI != EPI_WGRAD) {
-    if constexpr (HAS_RES || HAS_H || HAS_ROW) {
+  float colacc[FN][4];
 #pragma unroll
-      for (int i = 0; i < PD && i < FME; ++i) load_band(i);
-    }
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) colacc[j][v] = 0.f;
+
+  // Band by band: wait for the band's inputs, read them in the accumulator
+  // layout, hand the slot to the band PDS ahead, combine, pack to bf16 and
+  // store through the staging area. The hardware retires loads and stores
+  // of a wave in order through one counter; the wait for band i allows
+  // exactly the operations issued after band i's input loads to be pending.
+  auto run_bands = [&](auto in_tag) {
+    constexpr bool IN = decltype(in_tag)::value;
+    constexpr int DM = IN ? 2 * NIN : 0;  // input loads per band
+    constexpr int ST = NOUT * PERL;       // stores per band
 #pragma unroll
     for (int i = 0; i < FME; ++i) {
-      if constexpr (HAS_RES || HAS_H || HAS_ROW) {
-        if (i + PD < FME) load_band(i + PD);
+      u32x2 rin[FN], hin[FN];
+      if constexpr (IN) {
+        // Operations issued after band i's loads: the bands issued at the
+        // start after it, then per earlier band its successor's loads (if
+        // any) and its stores.
+        int after = 0;
+        if (i < PDS) {
+          for (int b2 = i + 1; b2 < PDS; ++b2) after += DM;
+          for (int k = 0; k < i; ++k) after += (k + PDS < FME ? DM : 0) + ST;
+        } else {
+          after = ST;
+          for (int k = i - PDS + 1; k < i; ++k) after += (k + PDS < FME ? DM : 0) + ST;
+        }
+        sched_fence();
+        wait_vmcnt_le(after);
+        sched_fence();
+        const unsigned char* slot = sIn + (i % PDS) * (NIN * 2048);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if constexpr (HAS_RES) rin[j] = *reinterpret_cast<const u32x2*>(slot + epi_acc_off(j, lane));
+          if constexpr (HAS_H) hin[j] = *reinterpret_cast<const u32x2*>(slot + 2048 + epi_acc_off(j, lane));
+        }
+        if (i + PDS < FME) {
+          wait_lgkmcnt0();  // the slot's reads have returned before it is refilled
+          issue_band(i + PDS);
+        }
       }
-      sched_fence();  // keep each band's work together: bounds live registers
       float rs = 1.0f;  // 1 / rms_g, 1 / rowdiv, or the RMSNorm-backward coefficient
       if constexpr (ORMS) rs = sRow[rb + 16 * i + fr];
       if constexpr (EPI == EPI_STORE) rs = 1.0f / rowv[i];
@@ -846,8 +1070,8 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       for (int j = 0; j < FN; ++j) {
         float o[NOUT][4];
         float rv[4] = {0.f, 0.f, 0.f, 0.f}, hv[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (HAS_RES) unpack4(rin[i][j], rv);
-        if constexpr (HAS_H) unpack4(hin[i][j], hv);
+        if constexpr (IN && HAS_RES) unpack4(rin[j], rv);
+        if constexpr (IN && HAS_H) unpack4(hin[j], hv);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float x = LR_E(0, i, j)[v];
@@ -887,14 +1111,21 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
         }
       }
 #pragma unroll
-      for (int q = 0; q < NOUT; ++q) {
-        void* cq = (EPI == EPI_STORE) ? pick3(g.c, slot) : pick3(g.c, q);
-        const int64_t lq = (EPI == EPI_STORE) ? pick3(g.ldc, slot) : pick3(g.ldc, q);
-        put_band(i, pk[q], cq, lq);
-      }
+      for (int q = 0; q < NOUT; ++q) put_band(i, pk[q], outs[q], cq[q], lq[q], in_tag);
+    }
+  };
+  if constexpr (EPI != EPI_WGRAD) {
+    if constexpr (NIN == 0) {
+      run_bands(std::false_type{});
+    } else if constexpr (EPI == EPI_STORE) {
+      if (in_on)
+        run_bands(std::true_type{});
+      else
+        run_bands(std::false_type{});
+    } else {
+      run_bands(std::true_type{});
     }
   }
-
 
   if constexpr (EPI == EPI_RMSBWD) {
     // This wave's column sums: the 16 lanes holding the same columns add
@@ -942,7 +1173,10 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
 
   if constexpr (EPI == EPI_RMSBWD) {
     const float* sCol = reinterpret_cast<const float*>(lds + TL::NWAVE * epi_wave_bytes<TL>());
-    __syncthreads();
+    // A bare barrier: the column sums are in LDS; the band stores may
+    // still be in flight.
+    wait_lgkmcnt0();
+    block_barrier();
     for (int c = tid; c < BN; c += TL::NT) {
       float sum = 0.f;
 #pragma unroll

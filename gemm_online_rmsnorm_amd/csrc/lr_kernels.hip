@@ -125,7 +125,7 @@ using PS256x128 = Tile2<256, 256, 32, 2, 4, 3, 2>;
 template <class TL, int NPAIR, uint32_t MC, int EPI>
 static hipError_t launch2(const GemmDesc& d, int groups, hipStream_t s) {
   auto kern = gemm2_kernel<TL, NPAIR, MC, EPI>;
-  constexpr int lds = gemm2_lds_bytes<TL, NPAIR>();
+  constexpr int lds = gemm2_lds_bytes<TL, NPAIR, EPI>();
   static_assert(lds <= 160 * 1024, "LDS budget exceeded");
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
@@ -210,6 +210,12 @@ static bool eligible2(int op, const GemmDesc& d, int groups, int bk) {
     if (operand_extent(bmc, d.ldb[p], d.N, d.K) >= ((int64_t)1 << 31)) return false;
   }
   if (op == OP_NT_ORMS && d.n_panels > 1 && d.panel_width % bk != 0) return false;
+  // The epilogue addresses a tile's outputs and element inputs with 32-bit
+  // byte offsets from the tile origin.
+  const int64_t ld_max = (int64_t)1 << 21;
+  for (int p = 0; p < 3; ++p)
+    if (d.ldc[p] >= ld_max) return false;
+  if (d.ldres >= ld_max || d.ldh >= ld_max) return false;
   return true;
 }
 
