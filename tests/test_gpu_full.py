@@ -20,12 +20,24 @@ WGRADS = ("dgamma1", "dgamma2", "dA_qkv", "dB_q", "dB_k", "dB_v", "dA_o", "dB_o"
           "dB_g", "dB_u", "dA_dn", "dB_dn")
 
 
+# Ragged variants of the 16384-token shapes: the token count leaves a
+# partial 256-row tile whose last 16-row band is half full, and d, r and d_ff
+# leave partial column tiles, so the large tiles' epilogues (band inputs,
+# stores, column sums) and the split gate/up tile run with rows and columns
+# past the matrix. All sizes stay multiples of 64.
+RAGGED = {
+    "1B-ragged-P2": synth.config(2).replace(name="1B-ragged-P2", T=16008, d=1920, r=448,
+                                            F=5568, D=1920, P=2, heads=16),
+    "30B-rank0of4-ragged": synth.config(5).replace(name="30B-rank0of4-ragged", T=16008),
+}
+
+
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5] + list(RAGGED))
 def test_full_workload_parity(cfg):
     torch = gpu_or_skip()
     from gemm_online_rmsnorm_amd.runner import BlockRun
-    s = synth.config(cfg)
+    s = RAGGED[cfg] if isinstance(cfg, str) else synth.config(cfg)
     say(f"[case] full workload {cfg}: {s.name} T={s.T} d={s.d} r={s.r} F={s.F} D={s.D} P={s.P}")
     t0 = time.time()
     inputs = synth.make_inputs(s)

@@ -31,14 +31,18 @@ def _host(t):
 LAYOUT = {"NT": 0, "NN": 1, "TN": 2}
 
 
+# bf16 products whose K is a multiple of 64 (32 for the gate/up pair) and
+# whose N is a multiple of 8 run on the pipelined engine; the others on the
+# general one. Each test covers both.
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
 @pytest.mark.parametrize("G", [1, 3])
-def test_grouped_gemm_layouts(dtype, layout, G):
+@pytest.mark.parametrize("K", [136, 128])
+def test_grouped_gemm_layouts(dtype, layout, G, K):
     torch = gpu_or_skip()
     import gemm_online_rmsnorm_amd as lr
-    rng = np.random.default_rng(100 * (dtype == "bf16") + 10 * LAYOUT[layout] + G)
-    M, N, K = 296, 200, 136
+    rng = np.random.default_rng(100 * (dtype == "bf16") + 10 * LAYOUT[layout] + G + K)
+    M, N = 296, 200
     xs = (K, M) if layout == "TN" else (M, K)
     ws = (N, K) if layout == "NT" else (K, N)
     pairs_h = [(_rand(rng, xs, dtype), _rand(rng, ws, dtype, 1 / np.sqrt(K))) for _ in range(G)]
@@ -59,11 +63,14 @@ def test_grouped_gemm_layouts(dtype, layout, G):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("layout", ["NT", "NN"])
-def test_gemm_epilogues(dtype, layout):
+@pytest.mark.parametrize("shape", [(264, 136, 72), (264, 136, 64), (4088, 4040, 64)])
+def test_gemm_epilogues(dtype, layout, shape):
+    """Residual and row-scale epilogues; the last shape runs 256 x 256 tiles
+    with a partial last row band and a partial last column tile."""
     torch = gpu_or_skip()
     import gemm_online_rmsnorm_amd as lr
-    rng = np.random.default_rng(7)
-    M, N, K = 264, 136, 72
+    rng = np.random.default_rng(7 + shape[2])
+    M, N, K = shape
     dl = lr.LR_BF16 if dtype == "bf16" else lr.LR_F32
     tol = BF16_TOL if dtype == "bf16" else F32_TOL
     x = _rand(rng, (M, K), dtype)
@@ -87,11 +94,14 @@ def test_gemm_epilogues(dtype, layout):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_swiglu_pair(dtype):
+@pytest.mark.parametrize("shape", [(300, 344, 80), (300, 344, 96), (4104, 2056, 96)])
+def test_swiglu_pair(dtype, shape):
+    """The last shape runs the split gate/up tile (256 rows x 128 gate + 128
+    up columns) with partial last row and column tiles."""
     torch = gpu_or_skip()
     import gemm_online_rmsnorm_amd as lr
-    rng = np.random.default_rng(11)
-    M, N, K = 300, 344, 80
+    rng = np.random.default_rng(11 + shape[2])
+    M, N, K = shape
     xg, xu = _rand(rng, (M, K), dtype), _rand(rng, (M, K), dtype)
     wg = _rand(rng, (N, K), dtype, 1 / np.sqrt(K))
     wu = _rand(rng, (N, K), dtype, 1 / np.sqrt(K))
