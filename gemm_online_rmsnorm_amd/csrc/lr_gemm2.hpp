@@ -719,11 +719,15 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   wait_lgkmcnt0();
   sched_fence();
 
-  for (int kt = 0; kt < nk; ++kt) {
+  // One K-tile. Fragment buffer of sub-step q of K-tile kt: (kt Q + q) & 1,
+  // i.e. (q + B0) & 1 with B0 = (kt Q) & 1; with an odd sub-step count the
+  // loop runs K-tiles in pairs so that B0 stays a constant.
+  auto ktile = [&](int kt, auto b0_tag) {
+    constexpr int B0 = decltype(b0_tag)::value;
     const unsigned char* st = stage_ptr(kt % S);
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-      const int buf = q & 1;
+      const int buf = (q + B0) & 1;
       // Nothing is scheduled across this wait in either direction: the
       // fragments of sub-step q (some read by inline assembly the compiler
       // does not track) are in registers only after it.
@@ -747,18 +751,6 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
         interleave<NDS, L, FM * FN>();
       }
     }
-    if constexpr (Q & 1) {
-      // An odd sub-step count leaves the next K-tile's first fragments in
-      // buffer 1; the loop reads sub-step 0 from buffer 0. The copy waits
-      // for the reads to land.
-      sched_fence();
-      wait_lgkmcnt0();
-      sched_fence();
-#pragma unroll
-      for (int i = 0; i < FM; ++i) fa[0][i] = fa[1][i];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) fb[0][j] = fb[1][j];
-    }
     if constexpr (ORMS) {
       if (++in_panel == g.panel_ktiles || kt == nk - 1) {
 #pragma unroll
@@ -777,6 +769,14 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     sched_fence();
     wait_lgkmcnt0();
     sched_fence();
+  };
+  if constexpr (Q & 1) {
+    for (int kt = 0; kt < nk; kt += 2) {
+      ktile(kt, std::integral_constant<int, 0>{});
+      if (kt + 1 < nk) ktile(kt + 1, std::integral_constant<int, 1>{});
+    }
+  } else {
+    for (int kt = 0; kt < nk; ++kt) ktile(kt, std::integral_constant<int, 0>{});
   }
   // The last fragment reads (of a stage no MFMA uses, or before the loop
   // with no K-tile at all) and the empty-range loads past the last K-tile
