@@ -94,10 +94,12 @@ def test_gemm_epilogues(dtype, layout, shape):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("shape", [(300, 344, 80), (300, 344, 96), (4104, 2056, 96)])
+@pytest.mark.parametrize("shape", [(300, 344, 80), (300, 344, 96), (4104, 2056, 96),
+                                   (4104, 2056, 128)])
 def test_swiglu_pair(dtype, shape):
-    """The last shape runs the split gate/up tile (256 rows x 128 gate + 128
-    up columns) with partial last row and column tiles."""
+    """The last two shapes run the split gate/up tile (256 rows x 128 gate +
+    128 up columns) with partial last row and column tiles, over an odd and
+    an even number of k-tiles."""
     torch = gpu_or_skip()
     import gemm_online_rmsnorm_amd as lr
     rng = np.random.default_rng(11 + shape[2])
