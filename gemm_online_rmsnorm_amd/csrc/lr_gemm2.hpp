@@ -441,15 +441,19 @@ constexpr int epi_nin() {
          (EPI == EPI_RMSBWD ? 1 : 0);
 }
 // Split tiles hand half of their accumulators over through LDS: in one
-// round, or in two rounds of a quarter each when band-input slots must fit
-// beside the exchange area.
-template <int EPI>
+// round, or in two rounds of a quarter each when the band-input slots would
+// not fit beside a one-round exchange area in the ring.
+template <class TL, int EPI>
 constexpr int epi_xch_rounds() {
-  return epi_nin<EPI>() > 0 ? 2 : 1;
+  constexpr int one = TL::NWAVE * (TL::FM / 2) * TL::FN * 4 * 64 * 4;
+  constexpr int fme = TL::FM / 2;
+  constexpr int pds = (epi_nin<EPI>() == 2 ? 3 : 4) < fme ? (epi_nin<EPI>() == 2 ? 3 : 4) : fme;
+  constexpr int slots = TL::NWAVE * pds * epi_nin<EPI>() * 2048;
+  return (epi_nin<EPI>() > 0 && one + slots > TL::NSTAGE * (2 * TL::BM + TL::BN) * TL::BK * 2) ? 2 : 1;
 }
 template <class TL, int EPI>
 constexpr int epi_xch_bytes() {
-  return TL::NSPLIT == 2 ? TL::NWAVE * (TL::FM / 2 / epi_xch_rounds<EPI>()) * TL::FN * 4 * 64 * 4 : 0;
+  return TL::NSPLIT == 2 ? TL::NWAVE * (TL::FM / 2 / epi_xch_rounds<TL, EPI>()) * TL::FN * 4 * 64 * 4 : 0;
 }
 // First byte of the band-input slots (1 KB aligned, after both areas above).
 template <class TL, int EPI>
@@ -471,9 +475,14 @@ constexpr int gemm2_body_bytes() {
   constexpr int epi = in_end > epi_area_bytes<TL>() ? in_end : epi_area_bytes<TL>();
   return ring > epi ? ring : epi;
 }
+// Per-panel row sums of squares and row scales of the Online RMSNorm.
+template <class TL, int EPI>
+constexpr int orms_bytes() {
+  return EPI == EPI_ORMS ? 8 * TL::BM * 4 + TL::BM * 4 : 0;
+}
 template <class TL, int NPAIR, int EPI>
 constexpr int gemm2_lds_bytes() {
-  return gemm2_body_bytes<TL, NPAIR, EPI>() + 8 * TL::BM * 4 /* sums of squares */ + TL::BM * 4;
+  return gemm2_body_bytes<TL, NPAIR, EPI>() + orms_bytes<TL, EPI>();
 }
 
 // ---------------------------------------------------------------------------
@@ -655,12 +664,16 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       // (slot i holds band (i + FM/2) mod FM), so that every wave keeps
       // slots 0 .. FM/2 - 1 and hands over the rest.
       const unsigned char* tAi = SPLITN ? (i < FM / 2 ? tA + srot : tA - srot) : tA;
-      if (amc)
-        fa[buf][i] = Opnd<BM, BK, TL::NWAVE, false>::read_frag(
-            tAi, Opnd<BM, BK, TL::NWAVE, false>::frag_off(w0m + 16 * i, s, lane));
-      else
+      if constexpr (MCMASK == 0u) {
         fa[buf][i] = Opnd<BM, BK, TL::NWAVE, true>::read_frag(
             tAi, Opnd<BM, BK, TL::NWAVE, true>::frag_off(w0m + 16 * i, s, lane));
+      } else if (amc) {
+        fa[buf][i] = Opnd<BM, BK, TL::NWAVE, false>::read_frag(
+            tAi, Opnd<BM, BK, TL::NWAVE, false>::frag_off(w0m + 16 * i, s, lane));
+      } else {
+        fa[buf][i] = Opnd<BM, BK, TL::NWAVE, true>::read_frag(
+            tAi, Opnd<BM, BK, TL::NWAVE, true>::frag_off(w0m + 16 * i, s, lane));
+      }
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -901,7 +914,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   }
 
   if constexpr (SPLITN) {
-    constexpr int NRD = epi_xch_rounds<EPI>();
+    constexpr int NRD = epi_xch_rounds<TL, EPI>();
     static_assert(XCH <= IN0, "the exchange area overlaps the input slots");
     static_assert(FME % NRD == 0, "exchange rounds split the bands");
     static_assert(XCH <= RING, "exchange area exceeds the ring");

@@ -121,6 +121,11 @@ using P3x128x128 = Tile2<128, 128, 32, 2, 4, 3>;
 // Gate and up products side by side: 256 x (128 gate + 128 up) B rows,
 // 8 waves each running one pair on a 128 x 64 wave tile.
 using PS256x128 = Tile2<256, 256, 32, 2, 4, 3, 2>;
+// The same pairing on 192 rows with k-tiles of 64 in two stages (all of the
+// LDS): every HBM-to-LDS load then covers whole 128-byte rows; loads of
+// 64-byte row halves, which k-tiles of 32 give, copy at half the rate and
+// bound the 256-row tile.
+using PS192x128 = Tile2<192, 256, 64, 2, 4, 2, 2>;
 
 template <class TL, int NPAIR, uint32_t MC, int EPI>
 static hipError_t launch2(const GemmDesc& d, int groups, hipStream_t s) {
@@ -247,6 +252,15 @@ static hipError_t launch_single(const GemmDesc& d, int groups, hipStream_t s) {
   }
 }
 
+// Tile choice of the gate/up pair GEMMs: 0 the 192-row split tile (k-tiles
+// of 64), 1 the 256-row split tile (k-tiles of 32), 2 the 128 x 128 two-pair
+// tile for grids that would leave CUs idle.
+static int split_tile(const GemmDesc& d) {
+  if (d.K % 64 == 0 && ntiles(d, 192, 128, 1) >= kCUs) return 0;
+  if (ntiles(d, 256, 128, 1) >= kCUs) return 1;
+  return 2;
+}
+
 // Weight gradients: 256 x 256 tiles when both output sides allow it, and a
 // split of K that minimises (waves of workgroups) / (split) plus a small cost
 // per extra split for the partial-sum traffic.
@@ -281,13 +295,18 @@ static hipError_t run_gemm2(int op, const GemmDesc& d, int groups, hipStream_t s
     case OP_NN_STORE: return launch_single<EPI_STORE, 2u>(d, groups, s);
     case OP_NN_RMSBWD: return launch_single<EPI_RMSBWD, 2u>(d, groups, s);
     case OP_NT_SWIGLU:
-      if (ntiles(d, 256, 128, 1) >= kCUs) return launch2<PS256x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
-      return launch2<P2x128x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
+      switch (split_tile(d)) {
+        case 0: return launch2<PS192x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
+        case 1: return launch2<PS256x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
+        default: return launch2<P2x128x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
+      }
     case OP_SWIGLU_BWD: return launch2<P3x128x128, 3, 32u, EPI_SWIGLU_BWD>(d, 1, s);
     case OP_SWIGLU_BWD2:
-      if (ntiles(d, 256, 128, 1) >= kCUs)
-        return launch2<PS256x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
-      return launch2<P2x128x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
+      switch (split_tile(d)) {
+        case 0: return launch2<PS192x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
+        case 1: return launch2<PS256x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
+        default: return launch2<P2x128x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
+      }
     default: return hipErrorInvalidValue;
   }
 }
@@ -301,7 +320,10 @@ static bool g_engine2 = true;
 void set_engine2(bool on) { g_engine2 = on; }
 
 int gemm2_tile_m(int op, const GemmDesc& d, int groups) {
-  if (op == OP_NT_SWIGLU || op == OP_SWIGLU_BWD2) return ntiles(d, 256, 128, 1) >= kCUs ? 256 : 128;
+  if (op == OP_NT_SWIGLU || op == OP_SWIGLU_BWD2) {
+    const int t = split_tile(d);
+    return t == 0 ? 192 : (t == 1 ? 256 : 128);
+  }
   if (op == OP_SWIGLU_BWD) return 128;
   return single_tile(d, groups) == 2 ? 128 : 256;
 }
