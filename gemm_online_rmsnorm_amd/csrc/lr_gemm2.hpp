@@ -923,16 +923,16 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     static_assert(XCH <= RING, "exchange area exceeds the ring");
     constexpr int NR = FME / NRD;
     const int partner = wm * TL::NWN + (wn + TL::NWN / 2) % TL::NWN;
-    float* xch = reinterpret_cast<float*>(lds);  // [NWAVE][NR][FN][4][64]
+    // [NWAVE][NR][FN][64 lanes][4]: a lane's four values of a fragment are
+    // one 16-byte access, a wave's instruction one contiguous 1 KB.
+    f32x4* xch = reinterpret_cast<f32x4*>(lds);
 #pragma unroll
     for (int rd = 0; rd < NRD; ++rd) {
 #pragma unroll
       for (int ii = 0; ii < NR; ++ii)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            xch[(((wave * NR + ii) * FN + j) * 4 + v) * 64 + lane] = acc[0][FME + rd * NR + ii][j][v];
+          xch[((wave * NR + ii) * FN + j) * 64 + lane] = acc[0][FME + rd * NR + ii][j];
       // A bare barrier: __syncthreads would also wait for the band-input
       // loads in flight.
       wait_lgkmcnt0();
@@ -942,15 +942,16 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
 #pragma unroll
       for (int ii = 0; ii < NR; ++ii)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j) {
+          const int i = rd * NR + ii;
+          const f32x4 oth = xch[((partner * NR + ii) * FN + j) * 64 + lane];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int i = rd * NR + ii;
             const float own = acc[0][i][j][v];
-            const float oth = xch[(((partner * NR + ii) * FN + j) * 4 + v) * 64 + lane];
-            acc[0][i][j][v] = pw ? oth : own;
-            acc[0][FME + i][j][v] = pw ? own : oth;
+            acc[0][i][j][v] = pw ? oth[v] : own;
+            acc[0][FME + i][j][v] = pw ? own : oth[v];
           }
+        }
       wait_lgkmcnt0();
       block_barrier();  // the next round and the staging area reuse the exchange area
     }
