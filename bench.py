@@ -44,6 +44,9 @@ def _parse():
                     help="tokens of the workload the CPU oracle runs for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true", help="also print the per-kernel table")
+    ap.add_argument("--tp-split", type=int, default=0, metavar="k",
+                    help="instead of the block step: time one rank's GEMMs of the config's "
+                         "block under the vanilla and the bottleneck-aware split over k ranks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"first make one device copy of {COPY_BYTES} bytes, the reference "
                          "rocprofv3 byte counters are scaled by")
@@ -74,6 +77,37 @@ def cpu_baseline(s, inputs, rows):
                       f"incl. weight grads, numpy float64 (OpenBLAS)"}
 
 
+def tp_split_main(args, s):
+    """One JSON line: one rank's GEMM time, TFLOP/s and arithmetic intensity
+    under the vanilla and the bottleneck-aware split of the config's block
+    over k ranks (same kernels, synthetic operands), and the all-reduce
+    values per token each split sends."""
+    from gemm_online_rmsnorm_amd import tp_split as tps
+    k = args.tp_split
+    if s.dtype != "bf16" or s.partials or s.d % k or s.r % k or s.F % k:
+        print(f"--tp-split needs a bf16 full-block config whose d, r, d_ff split {k} ways",
+              file=sys.stderr)
+        sys.exit(2)
+    print(f"[bench] tp split k={k} of {s.name}", file=sys.stderr, flush=True)
+    out = {"metric": f"one rank's block GEMMs under tensor parallelism over {k} GPUs",
+           "unit": "ms", "higher_is_better": False, "n_gpus": 1, "dtype": "bf16",
+           "data": "synthetic", "config": {"workload": f"{s.name} block, rank 0 of {k}",
+                                           "tokens": s.T, "d": s.d, "r": s.r, "d_ff": s.F}}
+    for split, fn in (("vanilla", tps.vanilla_gemms), ("bottleneck", tps.btp_gemms)):
+        rows = tps.time_split(fn(s.T, s.d, s.r, s.F, k))
+        summ = tps.summarize(rows, MFMA_BF16_PEAK_TFLOPS)
+        summ["allreduce_values_per_token"] = tps.allreduce_values_per_token(
+            "vanilla" if split == "vanilla" else "btp", s.d, s.r, s.F)
+        summ["gemms"] = [{k2: v for k2, v in r.items() if k2 not in ("flops", "bytes")}
+                         for r in rows]
+        out[split] = summ
+    out["value"] = out["bottleneck"]["ms"]
+    out["mlp_intensity_ratio"] = round(out["bottleneck"]["mlp"]["flop_per_byte"]
+                                       / out["vanilla"]["mlp"]["flop_per_byte"], 2)
+    out["speedup"] = round(out["vanilla"]["ms"] / out["bottleneck"]["ms"], 3)
+    print(json.dumps(out))
+
+
 def main():
     args = _parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -96,6 +130,9 @@ def main():
         sys.exit(1)
     lr._lib.load()
     s = synth.config(args.config)
+    if args.tp_split:
+        tp_split_main(args, s)
+        return
     print(f"[bench] workload {s.name} T={s.T} d={s.d} r={s.r} F={s.F} D={s.D} P={s.P}",
           file=sys.stderr, flush=True)
     inputs = synth.make_inputs(s)

@@ -104,11 +104,7 @@ def block_bwd(shape, W, X, O, saved, dY, dQ, dK, dV, dX, dO, grads, stage=LR_STA
         nbytes, _stream(stream, X.device)))
 
 
-def grouped_lowrank_gemm(pairs, dtype, layout=LR_LAYOUT_NT, epilogue=LR_EPI_NONE,
-                         stream=None) -> None:
-    """lr_grouped_lowrank_gemm. pairs: list of dicts with M, N, K, X, W, Y,
-    optional ldx, ldw, ldy (default: the contiguous row lengths), aux, ldaux."""
-    lib = _lib.load()
+def _pair_array(pairs, layout):
     arr = (_lib.lr_gemm_pair * len(pairs))()
     dev = None
     for i, p in enumerate(pairs):
@@ -119,8 +115,30 @@ def grouped_lowrank_gemm(pairs, dtype, layout=LR_LAYOUT_NT, epilogue=LR_EPI_NONE
         arr[i] = _lib.lr_gemm_pair(M, N, K, _ptr(p["X"]), ldx, _ptr(p["W"]), ldw, _ptr(p["Y"]),
                                    p.get("ldy", N), _ptr(aux), p.get("ldaux", N))
         dev = p["X"].device
-    _lib.check(lib.lr_grouped_lowrank_gemm(len(pairs), arr, dtype, layout, epilogue,
-                                           _stream(stream, dev)))
+    return arr, dev
+
+
+def grouped_lowrank_gemm(pairs, dtype, layout=LR_LAYOUT_NT, epilogue=LR_EPI_NONE,
+                         stream=None, ws=None) -> None:
+    """lr_grouped_lowrank_gemm (lr_grouped_lowrank_gemm_ws when a workspace
+    tensor is given). pairs: list of dicts with M, N, K, X, W, Y, optional
+    ldx, ldw, ldy (default: the contiguous row lengths), aux, ldaux."""
+    lib = _lib.load()
+    arr, dev = _pair_array(pairs, layout)
+    if ws is None:
+        _lib.check(lib.lr_grouped_lowrank_gemm(len(pairs), arr, dtype, layout, epilogue,
+                                               _stream(stream, dev)))
+    else:
+        _lib.check(lib.lr_grouped_lowrank_gemm_ws(len(pairs), arr, dtype, layout, epilogue,
+                                                  _ptr(ws), ws.numel() * ws.element_size(),
+                                                  _stream(stream, dev)))
+
+
+def grouped_lowrank_gemm_workspace_bytes(pairs, dtype, layout) -> int:
+    """lr_grouped_lowrank_gemm_workspace_bytes for these pairs."""
+    lib = _lib.load()
+    arr, _ = _pair_array(pairs, layout)
+    return int(lib.lr_grouped_lowrank_gemm_workspace_bytes(len(pairs), arr, dtype, layout))
 
 
 def online_rmsnorm_gemm(X, gamma, A, out, *, n_panels=1, d_norm=None, eps=1e-5, rms_out=None,

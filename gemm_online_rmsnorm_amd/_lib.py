@@ -28,7 +28,8 @@ LR_EPI_NONE, LR_EPI_ADD_RESIDUAL, LR_EPI_SWIGLU_PAIR, LR_EPI_ROW_SCALE = 0, 1, 2
 # Every function include/lr_block.h declares.
 EXPORTS = (
     "lr_block_workspace_bytes", "lr_block_fwd", "lr_block_bwd",
-    "lr_grouped_lowrank_gemm", "lr_online_rmsnorm_gemm_workspace_bytes",
+    "lr_grouped_lowrank_gemm", "lr_grouped_lowrank_gemm_workspace_bytes",
+    "lr_grouped_lowrank_gemm_ws", "lr_online_rmsnorm_gemm_workspace_bytes",
     "lr_online_rmsnorm_gemm", "lr_profile_enable", "lr_profile_collect", "lr_last_error",
     "lr_version",
 )
@@ -98,6 +99,12 @@ def load(path: str | None = None):
     lib.lr_grouped_lowrank_gemm.argtypes = [c_int32, POINTER(lr_gemm_pair), c_int32, c_int32,
                                             c_int32, c_void_p]
     lib.lr_grouped_lowrank_gemm.restype = c_int32
+    lib.lr_grouped_lowrank_gemm_workspace_bytes.argtypes = [c_int32, POINTER(lr_gemm_pair),
+                                                            c_int32, c_int32]
+    lib.lr_grouped_lowrank_gemm_workspace_bytes.restype = c_size_t
+    lib.lr_grouped_lowrank_gemm_ws.argtypes = [c_int32, POINTER(lr_gemm_pair), c_int32, c_int32,
+                                               c_int32, c_void_p, c_size_t, c_void_p]
+    lib.lr_grouped_lowrank_gemm_ws.restype = c_int32
     lib.lr_online_rmsnorm_gemm_workspace_bytes.argtypes = [c_int64, c_int64, c_int32]
     lib.lr_online_rmsnorm_gemm_workspace_bytes.restype = c_size_t
     lib.lr_online_rmsnorm_gemm.argtypes = [

@@ -945,8 +945,48 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
   return LR_OK;
 }
 
+namespace {
+// Validates a grouped call and builds its descriptor and operation.
+int grouped_desc(int32_t G, const lr_gemm_pair* pairs, int32_t dtype, int32_t layout,
+                 int32_t epilogue, lr::GemmDesc& g, int& op, int& groups);
+}  // namespace
+
 int lr_grouped_lowrank_gemm(int32_t G, const lr_gemm_pair* pairs, int32_t dtype, int32_t layout,
                             int32_t epilogue, void* stream) {
+  lr::GemmDesc g;
+  int op = 0, groups = 0;
+  RUN(grouped_desc(G, pairs, dtype, layout, epilogue, g, op, groups));
+  return gemm(op, dtype, g, groups, static_cast<hipStream_t>(stream), "grouped low-rank GEMM");
+}
+
+size_t lr_grouped_lowrank_gemm_workspace_bytes(int32_t G, const lr_gemm_pair* pairs,
+                                               int32_t dtype, int32_t layout) {
+  lr::GemmDesc g;
+  int op = 0, groups = 0;
+  if (grouped_desc(G, pairs, dtype, layout, LR_EPI_NONE, g, op, groups)) return 0;
+  if (op != lr::OP_TN_WGRAD) return 0;
+  return lr::wgrad_part_bytes(dtype, g, groups);
+}
+
+int lr_grouped_lowrank_gemm_ws(int32_t G, const lr_gemm_pair* pairs, int32_t dtype,
+                               int32_t layout, int32_t epilogue, void* ws, size_t ws_bytes,
+                               void* stream) {
+  lr::GemmDesc g;
+  int op = 0, groups = 0;
+  RUN(grouped_desc(G, pairs, dtype, layout, epilogue, g, op, groups));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t need = op == lr::OP_TN_WGRAD ? lr::wgrad_part_bytes(dtype, g, groups) : 0;
+  if (need == 0) return gemm(op, dtype, g, groups, st, "grouped low-rank GEMM");
+  RUN(check_ws(ws, ws_bytes, need));
+  ProfScope ps("grouped low-rank GEMM", st);
+  hipError_t e = lr::run_wgrad(dtype, g, groups, ws, ws_bytes, st);
+  if (e != hipSuccess) return hip_fail(e, "grouped low-rank GEMM");
+  return LR_OK;
+}
+
+namespace {
+int grouped_desc(int32_t G, const lr_gemm_pair* pairs, int32_t dtype, int32_t layout,
+                 int32_t epilogue, lr::GemmDesc& g, int& op, int& groups) {
   if (dtype != LR_F32 && dtype != LR_BF16)
     return fail(LR_ERR_INVALID_ARG, "dtype %d is neither LR_F32 nor LR_BF16", dtype);
   if (G < 1 || G > 3) return fail(LR_ERR_INVALID_ARG, "G = %d is out of range [1, 3]", G);
@@ -991,8 +1031,7 @@ int lr_grouped_lowrank_gemm(int32_t G, const lr_gemm_pair* pairs, int32_t dtype,
     if (epilogue == LR_EPI_ADD_RESIDUAL)
       return fail(LR_ERR_UNSUPPORTED, "the residual epilogue takes G = 1");
   }
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  lr::GemmDesc g;
+  g = lr::GemmDesc();
   g.M = (int)p0.M;
   g.N = (int)p0.N;
   g.K = (int)p0.K;
@@ -1010,8 +1049,7 @@ int lr_grouped_lowrank_gemm(int32_t G, const lr_gemm_pair* pairs, int32_t dtype,
   } else if (epilogue == LR_EPI_ROW_SCALE) {
     g.rowdiv = static_cast<const float*>(p0.aux);
   }
-  int op;
-  int groups = G;
+  groups = G;
   if (epilogue == LR_EPI_SWIGLU_PAIR) {
     op = lr::OP_NT_SWIGLU;
     groups = 1;
@@ -1022,8 +1060,9 @@ int lr_grouped_lowrank_gemm(int32_t G, const lr_gemm_pair* pairs, int32_t dtype,
   } else {
     op = lr::OP_TN_WGRAD;
   }
-  return gemm(op, dtype, g, groups, st, "grouped low-rank GEMM");
+  return LR_OK;
 }
+}  // namespace
 
 size_t lr_online_rmsnorm_gemm_workspace_bytes(int64_t N, int64_t d, int32_t dtype) {
   if ((dtype != LR_F32 && dtype != LR_BF16) || N < 1 || d < 1) return 0;

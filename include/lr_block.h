@@ -224,6 +224,24 @@ typedef struct {
 int lr_grouped_lowrank_gemm(int32_t G, const lr_gemm_pair* pairs, int32_t dtype,
                             int32_t layout, int32_t epilogue, void* stream);
 
+/* lr_grouped_lowrank_gemm with a caller-owned workspace. For the TN layout
+ * on the bf16 pipelined path, an output grid too small to fill the GPU
+ * (weight gradients of small factors, K = tokens) is computed as K-slices
+ * whose fp32 partial products go to ws and are then summed slice by slice
+ * in a fixed order, so results are deterministic; the slice count depends
+ * only on the shape. Every other layout, dtype or shape runs exactly as
+ * lr_grouped_lowrank_gemm and does not touch ws.
+ * lr_grouped_lowrank_gemm_workspace_bytes returns the bytes ws must hold
+ * for these pairs (0: none needed); ws must then be 256-byte aligned and
+ * must not be used by other work until the call's kernels have finished on
+ * `stream`. Errors as lr_grouped_lowrank_gemm, plus LR_ERR_WORKSPACE for a
+ * missing, short or misaligned workspace. */
+size_t lr_grouped_lowrank_gemm_workspace_bytes(int32_t G, const lr_gemm_pair* pairs,
+                                               int32_t dtype, int32_t layout);
+int lr_grouped_lowrank_gemm_ws(int32_t G, const lr_gemm_pair* pairs, int32_t dtype,
+                               int32_t layout, int32_t epilogue, void* ws, size_t ws_bytes,
+                               void* stream);
+
 /* Online RMSNorm fused into a down-projection (BOOST project page, "Three
  * supporting changes", Online RMSNorm; the correction alpha = RMS_local /
  * RMS_global of the awesome-system-papers summary):

@@ -161,6 +161,29 @@ def test_grouped_gemm_validation():
     assert lib.lr_grouped_lowrank_gemm(2, mixed, _lib.LR_BF16, 0, 0, None) == _lib.LR_ERR_UNSUPPORTED
 
 
+def test_grouped_gemm_workspace_variant_validation():
+    """The workspace variant validates like the plain call and checks the
+    workspace before launching anything (weight-gradient shape whose grid is
+    too small to fill the GPU: K is split)."""
+    lib = _ensure_built()
+    P = _lib.lr_gemm_pair
+    tn = (P * 1)(P(1024, 1024, 16384, 0x1000, 1024, 0x2000, 1024, 0x3000, 1024, None, 0))
+    need = lib.lr_grouped_lowrank_gemm_workspace_bytes(1, tn, _lib.LR_BF16, _lib.LR_LAYOUT_TN)
+    assert need > 0 and need % (1024 * 1024 * 4) == 0
+    # fp32 and the other layouts need none
+    assert lib.lr_grouped_lowrank_gemm_workspace_bytes(1, tn, _lib.LR_F32, _lib.LR_LAYOUT_TN) == 0
+    nt = (P * 1)(P(64, 64, 64, 0x1000, 64, 0x2000, 64, 0x3000, 64, None, 0))
+    assert lib.lr_grouped_lowrank_gemm_workspace_bytes(1, nt, _lib.LR_BF16, _lib.LR_LAYOUT_NT) == 0
+    f = lib.lr_grouped_lowrank_gemm_ws
+    assert f(0, tn, _lib.LR_BF16, _lib.LR_LAYOUT_TN, 0, 0x10000, need, None) == \
+        _lib.LR_ERR_INVALID_ARG
+    assert f(1, tn, _lib.LR_BF16, _lib.LR_LAYOUT_TN, 0, None, need, None) == _lib.LR_ERR_WORKSPACE
+    assert f(1, tn, _lib.LR_BF16, _lib.LR_LAYOUT_TN, 0, 0x10010, need, None) == \
+        _lib.LR_ERR_WORKSPACE
+    assert f(1, tn, _lib.LR_BF16, _lib.LR_LAYOUT_TN, 0, 0x10000, need - 256, None) == \
+        _lib.LR_ERR_WORKSPACE
+
+
 def test_online_rmsnorm_gemm_validation():
     lib = _ensure_built()
     f = lib.lr_online_rmsnorm_gemm

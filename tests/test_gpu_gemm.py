@@ -158,3 +158,33 @@ def test_online_rmsnorm_gemm(dtype, P):
     P_ref, ss_tot_ref = osh.norm_chunk_payload(g64, x64, A64)
     assert rel_err(_host(outp), P_ref) <= tol
     assert rel_err(_host(ssp), ss_tot_ref) <= 1e-5
+
+
+def test_grouped_gemm_workspace_split_k():
+    """The workspace variant of the grouped GEMM on a weight-gradient shape
+    whose output grid is small (K split into fp32 partial slices): oracle
+    parity and bitwise-identical repeats."""
+    torch = gpu_or_skip()
+    import gemm_online_rmsnorm_amd as lr
+    rng = np.random.default_rng(21)
+    M, N, K, G = 520, 264, 8192, 2
+    pairs_h = [(_rand(rng, (K, M), "bf16"), _rand(rng, (K, N), "bf16", 1 / np.sqrt(K)))
+               for _ in range(G)]
+    ys = [torch.empty(M, N, dtype=torch.float32, device="cuda") for _ in range(G)]
+    pairs = [dict(M=M, N=N, K=K, X=_dev(torch, x, "bf16"), W=_dev(torch, w, "bf16"), Y=y)
+             for (x, w), y in zip(pairs_h, ys)]
+    nb = lr.grouped_lowrank_gemm_workspace_bytes(pairs, lr.LR_BF16, lr.LR_LAYOUT_TN)
+    assert nb > 0
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    lr.grouped_lowrank_gemm(pairs, lr.LR_BF16, lr.LR_LAYOUT_TN, lr.LR_EPI_NONE, ws=ws)
+    torch.cuda.synchronize()
+    first = [y.clone() for y in ys]
+    ref = op.grouped_gemm("TN", pairs_h)
+    for y, r in zip(ys, ref):
+        e = rel_err(_host(y), r)
+        say(f"grouped TN split-K ({nb} B workspace): {e:.2e}")
+        assert e <= BF16_TOL
+    lr.grouped_lowrank_gemm(pairs, lr.LR_BF16, lr.LR_LAYOUT_TN, lr.LR_EPI_NONE, ws=ws)
+    torch.cuda.synchronize()
+    for y, f in zip(ys, first):
+        assert torch.equal(y, f)
