@@ -158,6 +158,40 @@ def online_rmsnorm_gemm(X, gamma, A, out, *, n_panels=1, d_norm=None, eps=1e-5, 
         _stream(stream, X.device)))
 
 
+def attn_shape(T, seq_len, n_heads, n_kv_heads=None, head_dim=128, rope_base=10000.0,
+               dtype=LR_BF16) -> _lib.lr_attn_shape:
+    return _lib.lr_attn_shape(T, seq_len, n_heads, n_kv_heads or n_heads, head_dim, dtype,
+                              rope_base)
+
+
+def attention_workspace_bytes(shape: _lib.lr_attn_shape, is_bwd: bool) -> int:
+    return int(_lib.load().lr_attention_workspace_bytes(ctypes.byref(shape), int(bool(is_bwd))))
+
+
+def _attn_ws(shape, is_bwd, ws, device):
+    if ws is None:
+        ws = torch.empty(max(attention_workspace_bytes(shape, is_bwd), 1), dtype=torch.uint8,
+                         device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def attention_fwd(shape, Q, K, V, O, lse, ws=None, stream=None) -> None:
+    """lr_attention_fwd: O [T, H*128] and lse [H, T] (fp32) from Q, K, V."""
+    lib = _lib.load()
+    ws, nbytes = _attn_ws(shape, False, ws, Q.device)
+    _lib.check(lib.lr_attention_fwd(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
+                                    _ptr(lse), _ptr(ws), nbytes, _stream(stream, Q.device)))
+
+
+def attention_bwd(shape, Q, K, V, O, dO, lse, dQ, dK, dV, ws=None, stream=None) -> None:
+    """lr_attention_bwd: dQ, dK, dV from Q, K, V, the forward's O and lse, and dO."""
+    lib = _lib.load()
+    ws, nbytes = _attn_ws(shape, True, ws, Q.device)
+    _lib.check(lib.lr_attention_bwd(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
+                                    _ptr(dO), _ptr(lse), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws),
+                                    nbytes, _stream(stream, Q.device)))
+
+
 def profile_enable(on: bool = True) -> None:
     """Start (True) or stop (False) per-kernel HIP-event timing in the library."""
     _lib.check(_lib.load().lr_profile_enable(int(bool(on))))

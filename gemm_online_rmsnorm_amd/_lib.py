@@ -30,7 +30,8 @@ EXPORTS = (
     "lr_block_workspace_bytes", "lr_block_fwd", "lr_block_bwd",
     "lr_grouped_lowrank_gemm", "lr_grouped_lowrank_gemm_workspace_bytes",
     "lr_grouped_lowrank_gemm_ws", "lr_online_rmsnorm_gemm_workspace_bytes",
-    "lr_online_rmsnorm_gemm", "lr_profile_enable", "lr_profile_collect", "lr_last_error",
+    "lr_online_rmsnorm_gemm", "lr_attention_workspace_bytes", "lr_attention_fwd",
+    "lr_attention_bwd", "lr_profile_enable", "lr_profile_collect", "lr_last_error",
     "lr_version",
 )
 
@@ -59,6 +60,12 @@ class lr_block_grads(ctypes.Structure):
 
 class lr_block_partials(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("P_qkv", "P_gu", "ss1", "ss2")]
+
+
+class lr_attn_shape(ctypes.Structure):
+    _fields_ = [("T", c_int64), ("seq_len", c_int64), ("n_heads", c_int32),
+                ("n_kv_heads", c_int32), ("head_dim", c_int32), ("dtype", c_int32),
+                ("rope_base", ctypes.c_double)]
 
 
 class lr_kernel_time(ctypes.Structure):
@@ -112,6 +119,16 @@ def load(path: str | None = None):
         c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
         c_size_t, c_void_p]
     lib.lr_online_rmsnorm_gemm.restype = c_int32
+    AS = POINTER(lr_attn_shape)
+    lib.lr_attention_workspace_bytes.argtypes = [AS, c_int32]
+    lib.lr_attention_workspace_bytes.restype = c_size_t
+    lib.lr_attention_fwd.argtypes = [AS, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_size_t, c_void_p]
+    lib.lr_attention_fwd.restype = c_int32
+    lib.lr_attention_bwd.argtypes = [AS, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                     c_void_p]
+    lib.lr_attention_bwd.restype = c_int32
     lib.lr_profile_enable.argtypes = [c_int32]
     lib.lr_profile_enable.restype = c_int32
     lib.lr_profile_collect.argtypes = [POINTER(lr_kernel_time), c_int32]

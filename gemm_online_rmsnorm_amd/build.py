@@ -16,7 +16,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblrblock.so")
-SOURCES = ("lr_kernels.hip", "lr_api.cpp")
+SOURCES = ("lr_kernels.hip", "lr_attention.hip", "lr_api.cpp")
 ARCH = os.environ.get("LRBLOCK_ARCH", "gfx950")
 
 

@@ -304,6 +304,170 @@ const char* lr_last_error(void) { return g_err.c_str(); }
 
 const char* lr_version(void) { return "lrblock 0.1 gfx950"; }
 
+// ---------------------------------------------------------------------------
+// Causal RoPE attention.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kAttnHeadDim = 128;
+
+int check_attn(const lr_attn_shape* s) {
+  if (!s) return fail(LR_ERR_INVALID_ARG, "shape is NULL");
+  if (s->T < 1 || s->seq_len < 1 || s->T > kMaxDim || s->seq_len > kMaxDim)
+    return fail(LR_ERR_INVALID_ARG, "T and seq_len must be in [1, 2^30]");
+  if (s->T % s->seq_len)
+    return fail(LR_ERR_INVALID_ARG, "T = %lld is not a multiple of seq_len = %lld",
+                (long long)s->T, (long long)s->seq_len);
+  if (s->n_heads < 1 || s->n_kv_heads < 1 || s->n_heads % s->n_kv_heads)
+    return fail(LR_ERR_INVALID_ARG, "n_heads = %d must be a positive multiple of n_kv_heads = %d",
+                s->n_heads, s->n_kv_heads);
+  if (s->dtype != LR_F32 && s->dtype != LR_BF16)
+    return fail(LR_ERR_INVALID_ARG, "dtype %d is neither LR_F32 nor LR_BF16", s->dtype);
+  if (s->dtype != LR_BF16)
+    return fail(LR_ERR_UNSUPPORTED, "attention runs in bf16 only");
+  if (s->head_dim < 1) return fail(LR_ERR_INVALID_ARG, "head_dim must be positive");
+  if (s->head_dim != kAttnHeadDim)
+    return fail(LR_ERR_UNSUPPORTED, "head_dim %d: only 128 is supported", s->head_dim);
+  if (!(s->rope_base > 1.0) || !std::isfinite(s->rope_base))
+    return fail(LR_ERR_INVALID_ARG, "rope_base must be finite and > 1");
+  // Byte offsets inside one sequence's head slice are 32-bit.
+  if ((int64_t)s->seq_len * s->n_heads * kAttnHeadDim * 2 >= ((int64_t)1 << 31))
+    return fail(LR_ERR_UNSUPPORTED, "seq_len * n_heads * 256 bytes must stay below 2^31");
+  if (s->T * (int64_t)s->n_heads * kAttnHeadDim >= ((int64_t)1 << 40))
+    return fail(LR_ERR_INVALID_ARG, "tensor too large");
+  return LR_OK;
+}
+
+struct AttnWs {
+  void* qr;
+  void* kr;
+  float* dsum;
+  size_t bytes;
+};
+
+AttnWs attn_carve(const lr_attn_shape* s, void* base, bool bwd) {
+  Carver c(base);
+  AttnWs w;
+  w.qr = c.take((size_t)s->T * s->n_heads * kAttnHeadDim * 2);
+  w.kr = c.take((size_t)s->T * s->n_kv_heads * kAttnHeadDim * 2);
+  w.dsum = bwd ? static_cast<float*>(c.take((size_t)s->T * s->n_heads * 4)) : nullptr;
+  w.bytes = c.off;
+  return w;
+}
+
+lr::AttnDesc attn_desc(const lr_attn_shape* s) {
+  lr::AttnDesc d;
+  d.T = (int)s->T;
+  d.seq_len = (int)s->seq_len;
+  d.H = s->n_heads;
+  d.Hkv = s->n_kv_heads;
+  d.rope_base = s->rope_base;
+  return d;
+}
+
+int check_attn_ws(const lr_attn_shape* s, void* ws, size_t ws_bytes, bool bwd) {
+  const size_t need = attn_carve(s, nullptr, bwd).bytes;
+  if (!ws || ws_bytes < need)
+    return fail(LR_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws_bytes, need);
+  if (!aligned16(ws)) return fail(LR_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+  return LR_OK;
+}
+
+// Rotated copies of Q and K into the workspace.
+int attn_rotate(const lr_attn_shape* s, const void* Q, const void* K, const AttnWs& w,
+                hipStream_t st) {
+  {
+    ProfScope ps("RoPE Q", st);
+    LR_HIP(lr::run_rope(Q, w.qr, (int)s->T, s->n_heads, (int)s->seq_len, s->rope_base, false, st),
+           "RoPE Q");
+  }
+  {
+    ProfScope ps("RoPE K", st);
+    LR_HIP(lr::run_rope(K, w.kr, (int)s->T, s->n_kv_heads, (int)s->seq_len, s->rope_base, false,
+                        st),
+           "RoPE K");
+  }
+  return LR_OK;
+}
+
+}  // namespace
+
+size_t lr_attention_workspace_bytes(const lr_attn_shape* shape, int32_t is_bwd) {
+  if (check_attn(shape) != LR_OK) return 0;
+  return attn_carve(shape, nullptr, is_bwd != 0).bytes;
+}
+
+int lr_attention_fwd(const lr_attn_shape* shape, const void* Q, const void* K, const void* V,
+                     void* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_attn(shape);
+  if (rc != LR_OK) return rc;
+  CHECK_PTR(Q);
+  CHECK_PTR(K);
+  CHECK_PTR(V);
+  CHECK_PTR(O);
+  if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(LR_ERR_INVALID_ARG, "lse is NULL or not 4-byte aligned");
+  rc = check_attn_ws(shape, ws, ws_bytes, false);
+  if (rc != LR_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const AttnWs w = attn_carve(shape, ws, false);
+  rc = attn_rotate(shape, Q, K, w, st);
+  if (rc != LR_OK) return rc;
+  lr::AttnDesc d = attn_desc(shape);
+  d.q = w.qr;
+  d.k = w.kr;
+  d.v = V;
+  d.o = O;
+  d.lse = lse;
+  ProfScope ps("attention fwd", st);
+  LR_HIP(lr::run_attn_fwd(d, st), "attention fwd");
+  return LR_OK;
+}
+
+int lr_attention_bwd(const lr_attn_shape* shape, const void* Q, const void* K, const void* V,
+                     const void* O, const void* dO, const float* lse, void* dQ, void* dK,
+                     void* dV, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_attn(shape);
+  if (rc != LR_OK) return rc;
+  CHECK_PTR(Q);
+  CHECK_PTR(K);
+  CHECK_PTR(V);
+  CHECK_PTR(O);
+  CHECK_PTR(dO);
+  CHECK_PTR(dQ);
+  CHECK_PTR(dK);
+  CHECK_PTR(dV);
+  if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(LR_ERR_INVALID_ARG, "lse is NULL or not 4-byte aligned");
+  rc = check_attn_ws(shape, ws, ws_bytes, true);
+  if (rc != LR_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const AttnWs w = attn_carve(shape, ws, true);
+  rc = attn_rotate(shape, Q, K, w, st);
+  if (rc != LR_OK) return rc;
+  lr::AttnDesc d = attn_desc(shape);
+  d.q = w.qr;
+  d.k = w.kr;
+  d.v = V;
+  d.o = const_cast<void*>(O);
+  d.dout = dO;
+  d.lse = const_cast<float*>(lse);
+  d.dsum = w.dsum;
+  d.dq = dQ;
+  d.dk = dK;
+  d.dv = dV;
+  {
+    ProfScope ps("attention bwd dQ", st);
+    LR_HIP(lr::run_attn_dq(d, st), "attention bwd dQ");
+  }
+  {
+    ProfScope ps("attention bwd dK dV", st);
+    LR_HIP(lr::run_attn_dkdv(d, st), "attention bwd dK dV");
+  }
+  return LR_OK;
+}
+
 int lr_profile_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (on) {

@@ -267,6 +267,65 @@ int lr_online_rmsnorm_gemm(int64_t T, int64_t d, int64_t N, int32_t n_panels, in
                            float* ss_out, int32_t emit_partial, int32_t dtype, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Causal self-attention with rotary position embedding (the attention core
+ * the block's forward leaves between Q, K, V and O). The BOOST pages do not
+ * define this operation: their block diagram runs the factorised layers
+ * around it, their related work cites FlashAttention and grouped-query
+ * attention, and the project page's scope section names grouped-query
+ * attention as a case the design is argued for. The library computes the
+ * LLaMA-2 family's textbook form:
+ *   - RoPE, half-split: for head dimension 128 and i < 64, the pair
+ *     (x_i, x_{i+64}) of a token at position p (0 .. seq_len - 1 within its
+ *     sequence) is rotated by the angle p * rope_base^(-2i/128), applied to
+ *     every head of Q and K;
+ *   - per sequence and query head h: O = softmax(q k^T / sqrt(128)) v with
+ *     keys after the query masked (causal), k and v from key/value head
+ *     h / (n_heads / n_kv_heads) (grouped-query attention; n_kv_heads =
+ *     n_heads is multi-head attention);
+ *   - LSE[h][t] = log(sum_j exp(q_t . k_j / sqrt(128))) over the unmasked
+ *     keys (natural log), saved for the backward;
+ *   - the backward of the above with respect to Q, K and V (the transposed
+ *     rotation applied to the gradients of the rotated q and k; the query
+ *     heads of a group add their key/value gradients).
+ * Layout: token-major, contiguous. Q, O, dO, dQ are [T][n_heads * 128];
+ * K, V, dK, dV are [T][n_kv_heads * 128]; head h occupies columns
+ * [128 h, 128 h + 128). The T tokens are T / seq_len sequences of seq_len
+ * consecutive tokens. LSE is [n_heads][T] fp32.
+ * Supported: dtype LR_BF16 (fp32 accumulation), head_dim 128; other values
+ * return LR_ERR_UNSUPPORTED. Requirements: T % seq_len == 0,
+ * n_heads % n_kv_heads == 0, seq_len * n_heads * 256 < 2^31, rope_base > 1
+ * and finite; bf16 pointers 16-byte aligned, LSE 4-byte aligned.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t T;          /* tokens (all sequences)                      */
+  int64_t seq_len;    /* tokens per sequence                         */
+  int32_t n_heads;    /* query heads                                 */
+  int32_t n_kv_heads; /* key/value heads, dividing n_heads           */
+  int32_t head_dim;   /* 128                                         */
+  int32_t dtype;      /* LR_BF16                                     */
+  double rope_base;   /* 10000 for LLaMA-2                           */
+} lr_attn_shape;
+
+/* Bytes of workspace lr_attention_fwd (is_bwd = 0) or lr_attention_bwd
+ * (is_bwd = 1) needs: the rotated Q and K, and for the backward the row sums
+ * rowsum(dO * O); 0 if the shape is invalid. The workspace carries nothing
+ * from the forward to the backward. */
+size_t lr_attention_workspace_bytes(const lr_attn_shape* shape, int32_t is_bwd);
+
+/* Forward: O and LSE from Q, K, V (all device memory; O and LSE are
+ * overwritten). ws: device workspace of lr_attention_workspace_bytes(shape,
+ * 0) bytes, 16-byte aligned. */
+int lr_attention_fwd(const lr_attn_shape* shape, const void* Q, const void* K, const void* V,
+                     void* O, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward: dQ, dK, dV (overwritten) from Q, K, V, the forward's O and LSE,
+ * and dO. ws: device workspace of lr_attention_workspace_bytes(shape, 1)
+ * bytes, 16-byte aligned. */
+int lr_attention_bwd(const lr_attn_shape* shape, const void* Q, const void* K, const void* V,
+                     const void* O, const void* dO, const float* lse, void* dQ, void* dK,
+                     void* dV, void* ws, size_t ws_bytes, void* stream);
+
 /* Measurement hook. While enabled, every kernel the library enqueues is
  * bracketed by a pair of HIP events recorded on the stream it is launched on
  * (events are created on first use and reused; no device memory is

@@ -186,3 +186,41 @@ def make_inputs(s: BlockShape, seed: int | None = None) -> dict[str, np.ndarray]
             v = round_to_bf16(v)
         out[name] = v
     return out
+
+
+# ---------------------------------------------------------------------------
+# Attention core (causal RoPE attention between the block's Q, K, V and O).
+# Shapes: LLaMA-2-7B has 32 heads of 128 (multi-head, 32 key/value heads);
+# the grouped-query case uses 8 key/value heads for 32 query heads.
+# Value distributions: Q, K, V, dO ~ N(0, 1), rounded to bf16.
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class AttnShape:
+    name: str
+    T: int               # tokens (sequences x seq_len)
+    seq_len: int
+    H: int               # query heads
+    Hkv: int             # key/value heads
+    dh: int = 128
+    base: float = 10000.0
+    seed: int = 0
+
+    @property
+    def n_seq(self) -> int:
+        return self.T // self.seq_len
+
+
+ATTN_7B = AttnShape("LLaMA-2-7B attention (4 x 4096 tokens, 32 heads of 128)", T=16384,
+                    seq_len=4096, H=32, Hkv=32)
+ATTN_7B_GQA = AttnShape("grouped-query attention (4 x 4096 tokens, 32 query / 8 kv heads)",
+                        T=16384, seq_len=4096, H=32, Hkv=8)
+
+
+def make_attn_inputs(s: AttnShape, seed: int | None = None) -> dict[str, np.ndarray]:
+    """Seeded Q [T, H dh], K and V [T, Hkv dh], dO [T, H dh] as bf16-exact
+    float32 arrays."""
+    rng = np.random.default_rng(s.seed if seed is None else seed)
+    out = {}
+    for name, heads in (("Q", s.H), ("K", s.Hkv), ("V", s.Hkv), ("dO", s.H)):
+        out[name] = round_to_bf16(rng.standard_normal((s.T, heads * s.dh), dtype=np.float32))
+    return out

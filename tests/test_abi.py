@@ -210,3 +210,56 @@ def test_online_rmsnorm_gemm_validation():
 def test_version_string():
     lib = _ensure_built()
     assert b"gfx950" in lib.lr_version()
+
+
+def test_attention_validation():
+    """The attention entry points reject unsupported or inconsistent shapes,
+    bad pointers and short workspaces before launching anything."""
+    lib = _ensure_built()
+    S = _lib.lr_attn_shape
+
+    def shape(**kw):
+        d = dict(T=8192, seq_len=4096, n_heads=32, n_kv_heads=8, head_dim=128,
+                 dtype=_lib.LR_BF16, rope_base=10000.0)
+        d.update(kw)
+        return S(**d)
+
+    def nbytes(s, bwd):
+        return lib.lr_attention_workspace_bytes(ctypes.byref(s), bwd)
+
+    ok = shape()
+    T, H, Hkv = 8192, 32, 8
+    need_f, need_b = nbytes(ok, 0), nbytes(ok, 1)
+    assert need_f >= T * (H + Hkv) * 128 * 2
+    assert need_b >= need_f + T * H * 4
+    fwd_args = (0x10000, 0x20000, 0x30000, 0x40000, 0x50000)
+
+    def fwd(s, ws=0x100000, wsb=None):
+        return lib.lr_attention_fwd(ctypes.byref(s), *fwd_args, ws,
+                                    need_f if wsb is None else wsb, None)
+
+    for kw, code in [(dict(seq_len=3000), _lib.LR_ERR_INVALID_ARG),   # T % seq_len
+                     (dict(n_kv_heads=5), _lib.LR_ERR_INVALID_ARG),   # H % Hkv
+                     (dict(n_heads=0), _lib.LR_ERR_INVALID_ARG),
+                     (dict(head_dim=64), _lib.LR_ERR_UNSUPPORTED),
+                     (dict(dtype=_lib.LR_F32), _lib.LR_ERR_UNSUPPORTED),
+                     (dict(dtype=5), _lib.LR_ERR_INVALID_ARG),
+                     (dict(rope_base=1.0), _lib.LR_ERR_INVALID_ARG),
+                     (dict(rope_base=float("inf")), _lib.LR_ERR_INVALID_ARG),
+                     (dict(T=1 << 20, seq_len=1 << 20, n_heads=64, n_kv_heads=8),
+                      _lib.LR_ERR_UNSUPPORTED)]:                       # 32-bit offsets
+        bad = shape(**kw)
+        assert nbytes(bad, 0) == 0, kw
+        assert fwd(bad) == code, kw
+    assert fwd(ok, wsb=need_f - 1) == _lib.LR_ERR_WORKSPACE
+    assert fwd(ok, ws=0x100008) == _lib.LR_ERR_WORKSPACE
+    assert fwd(ok, ws=None) == _lib.LR_ERR_WORKSPACE
+    assert lib.lr_attention_fwd(ctypes.byref(ok), 0x10008, 0x20000, 0x30000, 0x40000, 0x50000,
+                                0x100000, need_f, None) == _lib.LR_ERR_INVALID_ARG
+    assert lib.lr_attention_fwd(ctypes.byref(ok), 0x10000, 0x20000, 0x30000, 0x40000, 0x50002,
+                                0x100000, need_f, None) == _lib.LR_ERR_INVALID_ARG
+    bwd = lib.lr_attention_bwd
+    ptrs = [0x10000 * (i + 1) for i in range(9)]
+    assert bwd(ctypes.byref(ok), *ptrs, 0x100000, need_f, None) == _lib.LR_ERR_WORKSPACE
+    ptrs[7] = 0  # dK
+    assert bwd(ctypes.byref(ok), *ptrs, 0x100000, need_b, None) == _lib.LR_ERR_INVALID_ARG
