@@ -47,6 +47,9 @@ def _parse():
     ap.add_argument("--tp-split", type=int, default=0, metavar="k",
                     help="instead of the block step: time one rank's GEMMs of the config's "
                          "block under the vanilla and the bottleneck-aware split over k ranks")
+    ap.add_argument("--attention", choices=("mha", "gqa"), default=None,
+                    help="instead of the block step: causal RoPE attention fwd+bwd at the "
+                         "LLaMA-2-7B attention shape (mha: 32 kv heads, gqa: 8)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"first make one device copy of {COPY_BYTES} bytes, the reference "
                          "rocprofv3 byte counters are scaled by")
@@ -108,6 +111,126 @@ def tp_split_main(args, s):
     print(json.dumps(out))
 
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def attention_main(args):
+    """One JSON line: causal RoPE attention, forward + backward, at the
+    LLaMA-2-7B attention shape (4 sequences of 4096 tokens, 32 query heads
+    of 128). TFLOP/s counts the products one pass needs over the unmasked
+    (query, key) pairs: 4 * 128 flops per pair and head forward, 10 * 128
+    backward; the split backward kernels recompute the scores and dP."""
+    import numpy as np
+    import torch
+
+    import synth
+    import gemm_online_rmsnorm_amd as lr
+
+    s = synth.ATTN_7B_GQA if args.attention == "gqa" else synth.ATTN_7B
+    print(f"[bench] attention {s.name}", file=sys.stderr, flush=True)
+    inp = synth.make_attn_inputs(s)
+    dev = {k: torch.from_numpy(v).cuda().to(torch.bfloat16) for k, v in inp.items()}
+    Q, K, V, dO = dev["Q"], dev["K"], dev["V"], dev["dO"]
+    shape = lr.attn_shape(s.T, s.seq_len, s.H, s.Hkv, s.dh, s.base)
+    O = torch.empty_like(Q)
+    lse = torch.empty(s.H, s.T, dtype=torch.float32, device="cuda")
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    wsf = torch.empty(lr.attention_workspace_bytes(shape, False), dtype=torch.uint8,
+                      device="cuda")
+    wsb = torch.empty(lr.attention_workspace_bytes(shape, True), dtype=torch.uint8,
+                      device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        lr.attention_fwd(shape, Q, K, V, O, lse, ws=wsf, stream=stream)
+        lr.attention_bwd(shape, Q, K, V, O, dO, lse, dQ, dK, dV, ws=wsb, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    lr.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    lr.profile_enable(False)
+    prof = lr.profile_collect()
+
+    pairs = s.n_seq * s.seq_len * (s.seq_len + 1) / 2   # unmasked (query, key) pairs
+    per_pair = {"attention fwd": 4, "attention bwd dQ": 6, "attention bwd dK dV": 8}
+    kernels = []
+    for name, count, total in prof:
+        per = total / count
+        rec = {"kernel": name, "launches_per_step": count // args.steps, "ms": round(per, 4),
+               "step_ms": round(total / args.steps, 4)}
+        if name in per_pair:
+            fl = per_pair[name] * s.dh * pairs * s.H
+            rec["tflops"] = round(fl / (per * 1e-3) / 1e12, 1)
+        else:  # RoPE: read and write one tensor
+            heads = s.H if name.endswith("Q") else s.Hkv
+            rec["gbs"] = round(2 * s.T * heads * s.dh * 2 / (per * 1e-3) / 1e9, 1)
+        kernels.append(rec)
+    dom = max((k for k in kernels if "tflops" in k), key=lambda k: k["step_ms"])
+    flop = 14 * s.dh * pairs * s.H
+    tflops = flop / (ms * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import attention as oa
+        S, nh = s.seq_len, 2
+        grp = s.H // s.Hkv
+        sl = {n: inp[n][:S, :nh * s.dh] for n in ("Q", "dO")}
+        kv = {n: inp[n][:S, :s.dh] for n in ("K", "V")}
+        t0 = time.perf_counter()
+        oa.attention_forward(sl["Q"], kv["K"], kv["V"], S, nh, 1, s.dh, s.base)
+        oa.attention_backward(sl["Q"], kv["K"], kv["V"], sl["dO"], S, nh, 1, s.dh, s.base)
+        dt = time.perf_counter() - t0
+        cfl = 14 * s.dh * (S * (S + 1) / 2) * nh
+        cpu = {"value": round(cfl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": _blas_threads(),
+               "kind": "oracle", "seconds": round(dt, 2),
+               "sample": f"one sequence of {S} tokens, {nh} query heads sharing one "
+                         f"key/value head (grp {grp} in the workload), fwd+bwd, numpy float64"}
+
+    line = {
+        "metric": "causal RoPE attention fwd+bwd TFLOP/s",
+        "value": round(tflops, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian Q, K, V, dO)",
+        "config": {"workload": s.name, "tokens": s.T, "seq_len": s.seq_len, "heads": s.H,
+                   "kv_heads": s.Hkv, "head_dim": s.dh, "rope_base": s.base},
+        "mfma_peak_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {"kernel": dom["kernel"], "bound": "mfma", "achieved": dom["tflops"],
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dom["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "ms_per_launch": dom["ms"]},
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = _parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -129,6 +252,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     lr._lib.load()
+    if args.attention:
+        attention_main(args)
+        return
     s = synth.config(args.config)
     if args.tp_split:
         tp_split_main(args, s)

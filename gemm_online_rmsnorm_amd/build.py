@@ -18,6 +18,10 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblrblock.so")
 SOURCES = ("lr_kernels.hip", "lr_attention.hip", "lr_api.cpp")
 ARCH = os.environ.get("LRBLOCK_ARCH", "gfx950")
+# The attention backward keeps its dK/dV accumulators and K/V fragments in
+# registers past 256 VGPRs; the VGPR form of the MFMA instructions lets the
+# compiler hold them without copying through AGPRs on every iteration.
+EXTRA = {"lr_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def _hipcc() -> str:
@@ -39,7 +43,8 @@ def build(verbose: bool = False) -> str:
         def compile_one(src: str) -> str:
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
             lang = ["-x", "hip"] if src.endswith(".cpp") else []
-            cmd = [hipcc, *flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc, *flags(), *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src),
+                   "-o", obj]
             r = subprocess.run(cmd, capture_output=True, text=True)
             msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                             if "packed-fp32-ops" not in l)

@@ -342,6 +342,7 @@ struct AttnWs {
   void* qr;
   void* kr;
   float* dsum;
+  float* lse2;
   size_t bytes;
 };
 
@@ -351,6 +352,7 @@ AttnWs attn_carve(const lr_attn_shape* s, void* base, bool bwd) {
   w.qr = c.take((size_t)s->T * s->n_heads * kAttnHeadDim * 2);
   w.kr = c.take((size_t)s->T * s->n_kv_heads * kAttnHeadDim * 2);
   w.dsum = bwd ? static_cast<float*>(c.take((size_t)s->T * s->n_heads * 4)) : nullptr;
+  w.lse2 = bwd ? static_cast<float*>(c.take((size_t)s->T * s->n_heads * 4)) : nullptr;
   w.bytes = c.off;
   return w;
 }
@@ -454,6 +456,7 @@ int lr_attention_bwd(const lr_attn_shape* shape, const void* Q, const void* K, c
   d.dout = dO;
   d.lse = const_cast<float*>(lse);
   d.dsum = w.dsum;
+  d.lse2 = w.lse2;
   d.dq = dQ;
   d.dk = dK;
   d.dv = dV;

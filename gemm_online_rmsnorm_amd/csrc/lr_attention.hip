@@ -41,6 +41,7 @@
 
 #include <cmath>
 #include <mutex>
+#include <type_traits>
 
 #include "lr_common.hpp"
 #include "lr_gemm2.hpp"
@@ -107,16 +108,35 @@ __device__ __forceinline__ int xcd_item(int nwg) {
   return x * q + (x < rem ? x : rem) + pid / NXCD;
 }
 
+// 16-byte chunk c of row r of a streamed tile sits at chunk c ^ swz(r).
+// The sixteen rows of a 16-byte fragment read (rows r0 .. r0 + 15, one
+// logical chunk) land on sixteen distinct chunks, and so do the sixteen
+// (row, chunk) pairs each half-wave of a transposing read touches (rows
+// r0 + 0..7 or r0 + 8..15, chunks 2i and 2i + 1): both reads are free of
+// bank conflicts.
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
 // HBM-to-LDS copy of 64-row tiles of a [rows][128] bf16 head slice with
-// row stride ld: 16 blocks of 1 KB (4 rows each), four per wave.
+// row stride ld: 16 blocks of 1 KB (4 rows each), four per wave. The
+// per-lane offsets depend only on ld; the buffer resource (base and the
+// slice's extent, so rows past the end read zeros) is set per slice.
 struct TileDma {
 #if defined(__HIP_DEVICE_COMPILE__)
   __amdgpu_buffer_rsrc_t rs;
 #endif
   uint32_t off[4];
   uint32_t step;  // bytes between consecutive tiles
-  __device__ __forceinline__ void init(const bf16_t* base, int64_t ld, int rows, int lane,
-                                       int wave) {
+  __device__ __forceinline__ void init(int64_t ld, int lane, int wave) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int blk = 4 * v + wave;
+      const int r = 4 * blk + (lane >> 4);
+      const int c = (lane & 15) ^ swz(r);
+      off[v] = (uint32_t)(2 * ((int64_t)r * ld + 8 * c));
+    }
+    step = (uint32_t)wave_uniform((int)(2 * (int64_t)TR * ld));
+  }
+  __device__ __forceinline__ void set(const bf16_t* base, int64_t ld, int rows) {
     const int64_t nb = rows > 0 ? 2 * ((int64_t)(rows - 1) * ld + DH) : 0;
 #if defined(__HIP_DEVICE_COMPILE__)
     rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), (short)0, (int)nb,
@@ -124,14 +144,6 @@ struct TileDma {
 #else
     (void)base; (void)nb;
 #endif
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int blk = 4 * v + wave;
-      const int r = 4 * blk + (lane >> 4);
-      const int c = (lane & 15) ^ (r & 15);
-      off[v] = (uint32_t)(2 * ((int64_t)r * ld + 8 * c));
-    }
-    step = (uint32_t)wave_uniform((int)(2 * (int64_t)TR * ld));
   }
   __device__ __forceinline__ void issue(int tile, unsigned char* dst, int wave) const {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -147,42 +159,48 @@ struct TileDma {
 
 // HBM-to-LDS copy of 64 consecutive fp32 values (one per row of a tile),
 // issued by one wave; values past `n` read as zeros.
-struct RowDma {
+__device__ __forceinline__ void row_dma(const float* base, int n, int tile, unsigned char* dst,
+                                        int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __amdgpu_buffer_rsrc_t rs;
-#endif
-  __device__ __forceinline__ void init(const float* base, int n) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, 4 * n, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(base), (short)0, 4 * n, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LR_LPTR(dst), 4, (uint32_t)(4 * (TR * tile + lane)),
+                                           0, 0, 0);
 #else
-    (void)base; (void)n;
+  (void)base; (void)n; (void)tile; (void)dst; (void)lane;
 #endif
-  }
-  __device__ __forceinline__ void issue(int tile, unsigned char* dst, int lane) const {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LR_LPTR(dst), 4,
-                                             (uint32_t)(4 * (TR * tile + lane)), 0, 0, 0);
-#else
-    (void)tile; (void)dst; (void)lane;
-#endif
-  }
-};
+}
 
-// 16-byte fragment (row `r` of the tile, k = 32 st + 8g .. + 7).
-__device__ __forceinline__ u32x4 frag_rows(const unsigned char* tile, int r, int st, int g) {
-  return *reinterpret_cast<const u32x4*>(tile + r * ROWB + 16 * ((4 * st + g) ^ (r & 15)));
+// Per-lane byte offsets inside a tile. Row fragments: lane (g, s) reads
+// row 16 kf + s, logical chunk 4 st + g, at rowoff[st] + 4096 kf.
+__device__ __forceinline__ void row_offsets(int g, int s, uint32_t (&o)[4]) {
+#pragma unroll
+  for (int st = 0; st < 4; ++st) o[st] = (uint32_t)(s * ROWB + 16 * ((4 * st + g) ^ swz(s)));
+}
+// Column fragments: lane (g, s) reads columns 16 i + 4 (s & 3) .. + 3 of
+// rows 32 t + 4g + s / 4 and 16 rows below, at coloff[i] + 8192 t (+ 4096).
+__device__ __forceinline__ void col_offsets(int g, int s, uint32_t (&o)[8]) {
+  const int r0 = 4 * g + (s >> 2);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    o[i] = (uint32_t)(r0 * ROWB + 16 * ((2 * i + ((s >> 1) & 1)) ^ swz(r0)) + 8 * (s & 1));
+}
+
+// 16-byte row fragment at LDS byte `addr` + IMM.
+template <int IMM>
+__device__ __forceinline__ u32x4 frag_rows(const unsigned char* lds, uint32_t off) {
+  return *reinterpret_cast<const u32x4*>(lds + IMM + off);
 }
 
 // Transposed fragment: lane (g, s) receives column 16 i + s of tile rows
-// 32 t + 4g .. + 3 and 32 t + 16 + 4g .. + 3 (the permuted k-slots).
-__device__ __forceinline__ u32x4 frag_cols(const unsigned char* tile, int i, int t, int g,
-                                           int s) {
-  const int r = 32 * t + 4 * g + (s >> 2);
-  const int col = 16 * i + 4 * (s & 3);
-  const uint32_t a = lds_addr(tile + r * ROWB + 16 * ((col >> 3) ^ (r & 15)) + 2 * (col & 7));
+// 32 t + 4g .. + 3 and 32 t + 16 + 4g .. + 3 (the permuted k-slots); addr
+// is the lane's LDS address of column block i (coloff), IMM the tile's
+// offset plus 8192 t.
+template <int IMM>
+__device__ __forceinline__ u32x4 frag_cols(uint32_t addr) {
   bf16x4 lo, hi;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a));
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(a), "n"(16 * ROWB));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(addr), "n"(IMM));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(addr), "n"(IMM + 16 * ROWB));
   u32x4 r4;
   r4[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
   r4[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3));
@@ -191,7 +209,7 @@ __device__ __forceinline__ u32x4 frag_cols(const unsigned char* tile, int i, int
   return r4;
 }
 
-// Wait for this wave's LDS reads and tie the wait to the four fragments it
+// Wait for this wave's LDS reads and tie the wait to the fragments it
 // delivers: the transposing reads are inline assembly, so without the tie
 // the compiler could schedule a product that uses a fragment before the
 // wait.
@@ -211,6 +229,9 @@ __device__ __forceinline__ u32x4 pack_b(const f32x4& x0, const f32x4& x1) {
   r[3] = pack_bf16x2(x1[2], x1[3]);
   return r;
 }
+
+template <int V>
+using IC = std::integral_constant<int, V>;
 
 // Sixteen bytes of a row of a global [rows][ld] tensor, zero past `rows`.
 __device__ __forceinline__ u32x4 load_row16(const bf16_t* base, int64_t ld, int row, int rows,
@@ -303,12 +324,15 @@ struct FwdArgs {
 };
 
 constexpr int FBM = 128;
-constexpr int FWD_LDS = 4 * TILEB;
+constexpr int FWD_LDS = 4 * TILEB;  // K stages 0, 1; V stages 0, 1
+// The running row maximum is raised (and O and the row sum rescaled) only
+// when a tile's maximum exceeds it by more than this many powers of two;
+// probabilities then stay below 2^8, and the final normalisation uses the
+// same maximum, so the result is unchanged.
+constexpr float kRescaleLog2 = 8.0f;
 
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
-  unsigned char* sK = lds;
-  unsigned char* sV = lds + 2 * TILEB;
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int g = lane >> 4, s16 = lane & 15;
@@ -323,10 +347,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const int nkt = (qend + TR - 1) / TR;
 
   TileDma dk, dv;
-  dk.init(a.k + tok0 * ldk + hk * DH, ldk, a.seq_len, lane, wave);
-  dv.init(a.v + tok0 * ldk + hk * DH, ldk, a.seq_len, lane, wave);
-  dk.issue(0, sK, wave);
-  dv.issue(0, sV, wave);
+  dk.init(ldk, lane, wave);
+  dv.init(ldk, lane, wave);
+  dk.set(a.k + tok0 * ldk + hk * DH, ldk, a.seq_len);
+  dv.set(a.v + tok0 * ldk + hk * DH, ldk, a.seq_len);
+  dk.issue(0, lds, wave);
+  dv.issue(0, lds + 2 * TILEB, wave);
+
+  uint32_t roff[4], caddr[8];
+  row_offsets(g, s16, roff);
+  col_offsets(g, s16, caddr);
+  const uint32_t lbase = lds_addr(lds);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) caddr[i] += lbase;
 
   const bf16_t* qbase = a.q + tok0 * ldq + h * DH;
   u32x4 qf[2][4];
@@ -345,19 +378,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const float c = a.c;
   const bool live = qw < a.seq_len;
 
-  for (int j = 0; j < nkt; ++j) {
-    const int st = j & 1;
+  auto tile = [&](auto stc, int j) {
+    constexpr int ST = decltype(stc)::value;
+    constexpr int KO = ST * TILEB, VO = 2 * TILEB + ST * TILEB;
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     block_barrier();
     if (j + 1 < nkt) {
-      dk.issue(j + 1, sK + (st ^ 1) * TILEB, wave);
-      dv.issue(j + 1, sV + (st ^ 1) * TILEB, wave);
+      dk.issue(j + 1, lds + (ST ^ 1) * TILEB, wave);
+      dv.issue(j + 1, lds + 2 * TILEB + (ST ^ 1) * TILEB, wave);
     }
     const int k0 = j * TR;
-    if (!live || k0 > qw + 31) continue;  // every key after every query of this wave
-    const unsigned char* Ks = sK + st * TILEB;
-    const unsigned char* Vs = sV + st * TILEB;
+    if (!live || k0 > qw + 31) return;  // every key after every query of this wave
 
     f32x4 sc[2][4];
 #pragma unroll
@@ -368,7 +400,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     for (int stp = 0; stp < 4; ++stp)
 #pragma unroll
       for (int kf = 0; kf < 4; ++kf) {
-        const u32x4 kr = frag_rows(Ks, 16 * kf + s16, stp, g);
+        const u32x4 kr = frag_rows<0>(lds + KO + 4096 * kf, roff[stp]);
 #pragma unroll
         for (int f = 0; f < 2; ++f) sc[f][kf] = mma(kr, qf[f][stp], sc[f][kf]);
       }
@@ -391,9 +423,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) mx = fmaxf(mx, sc[f][kf][v]);
       mx = xg_max(mx);
-      const float alpha = fexp2((m[f] - mx) * c);
-      m[f] = mx;
-      const float mc = mx * c;
+      const bool grow = (mx - m[f]) * c > kRescaleLog2;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float alpha = grow ? fexp2((m[f] - mx) * c) : 1.0f;
+        m[f] = grow ? mx : m[f];
+        l[f] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[f][i] *= alpha;
+      }
+      const float mc = m[f] * c;
       float rs = 0.f;
 #pragma unroll
       for (int kf = 0; kf < 4; ++kf)
@@ -403,13 +441,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
           sc[f][kf][v] = p;
           rs += p;
         }
-      l[f] = l[f] * alpha + rs;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[f][i] *= alpha;
+      l[f] += rs;
     }
 
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    auto pv = [&](auto tc) {
+      constexpr int t = decltype(tc)::value;
       u32x4 pb[2];
 #pragma unroll
       for (int f = 0; f < 2; ++f) pb[f] = pack_b(sc[f][2 * t], sc[f][2 * t + 1]);
@@ -417,14 +453,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
       for (int i0 = 0; i0 < 8; i0 += 4) {
         u32x4 vt[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) vt[u] = frag_cols(Vs, i0 + u, t, g, s16);
+        for (int u = 0; u < 4; ++u) vt[u] = frag_cols<VO + 8192 * t>(caddr[i0 + u]);
         lds_wait(vt);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
           for (int f = 0; f < 2; ++f) o[f][i0 + u] = mma(vt[u], pb[f], o[f][i0 + u]);
       }
-    }
+    };
+    pv(IC<0>{});
+    pv(IC<1>{});
+  };
+  for (int j = 0; j < nkt; j += 2) {
+    tile(IC<0>{}, j);
+    if (j + 1 < nkt) tile(IC<1>{}, j + 1);
   }
 
   if (!live) return;
@@ -445,8 +487,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Backward, dQ. Block: 128 queries of one (sequence, head), 4 waves of 32;
-// key/value tiles stream as in the forward. First writes D = rowsum(dO * O)
-// for its rows.
+// key/value tiles stream as in the forward. First writes, for its rows,
+// D = rowsum(dO * O) and LSE * log2(e) for the dK/dV kernel.
 // ---------------------------------------------------------------------------
 struct BwdArgs {
   const bf16_t* q;     // rotated, [T][H * 128]
@@ -456,6 +498,7 @@ struct BwdArgs {
   const bf16_t* dout;  // its gradient [T][H * 128]
   const float* lse;    // [H][T]
   float* dsum;         // [H][T]: rowsum(dO * O)
+  float* lse2;         // [H][T]: LSE * log2(e)
   bf16_t* dq;          // [T][H * 128]
   bf16_t* dk;          // [T][Hkv * 128]
   bf16_t* dv;          // [T][Hkv * 128]
@@ -470,8 +513,6 @@ constexpr int DQ_LDS = 4 * TILEB;
 
 __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
-  unsigned char* sK = lds;
-  unsigned char* sV = lds + 2 * TILEB;
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int g = lane >> 4, s16 = lane & 15;
@@ -486,10 +527,19 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
   const int nkt = (qend + TR - 1) / TR;
 
   TileDma dk, dv;
-  dk.init(a.k + tok0 * ldk + hk * DH, ldk, a.seq_len, lane, wave);
-  dv.init(a.v + tok0 * ldk + hk * DH, ldk, a.seq_len, lane, wave);
-  dk.issue(0, sK, wave);
-  dv.issue(0, sV, wave);
+  dk.init(ldk, lane, wave);
+  dv.init(ldk, lane, wave);
+  dk.set(a.k + tok0 * ldk + hk * DH, ldk, a.seq_len);
+  dv.set(a.v + tok0 * ldk + hk * DH, ldk, a.seq_len);
+  dk.issue(0, lds, wave);
+  dv.issue(0, lds + 2 * TILEB, wave);
+
+  uint32_t roff[4], caddr[8];
+  row_offsets(g, s16, roff);
+  col_offsets(g, s16, caddr);
+  const uint32_t lbase = lds_addr(lds);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) caddr[i] += lbase;
 
   const int64_t hoff = tok0 * ldq + h * DH;
   u32x4 qf[2][4], df[2][4];
@@ -512,7 +562,10 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
     dsum[f] = xg_sum(part);
     const bool ok = row < a.seq_len;
     lse2[f] = ok ? a.lse[(int64_t)h * a.T + tok0 + row] * kLog2e : 0.f;
-    if (ok && g == 0) a.dsum[(int64_t)h * a.T + tok0 + row] = dsum[f];
+    if (ok && g == 0) {
+      a.dsum[(int64_t)h * a.T + tok0 + row] = dsum[f];
+      a.lse2[(int64_t)h * a.T + tok0 + row] = lse2[f];
+    }
   }
 
   f32x4 acc[2][8];
@@ -523,19 +576,18 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
   const float c = a.c;
   const bool live = qw < a.seq_len;
 
-  for (int j = 0; j < nkt; ++j) {
-    const int st = j & 1;
+  auto tile = [&](auto stc, int j) {
+    constexpr int ST = decltype(stc)::value;
+    constexpr int KO = ST * TILEB, VO = 2 * TILEB + ST * TILEB;
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     block_barrier();
     if (j + 1 < nkt) {
-      dk.issue(j + 1, sK + (st ^ 1) * TILEB, wave);
-      dv.issue(j + 1, sV + (st ^ 1) * TILEB, wave);
+      dk.issue(j + 1, lds + (ST ^ 1) * TILEB, wave);
+      dv.issue(j + 1, lds + 2 * TILEB + (ST ^ 1) * TILEB, wave);
     }
     const int k0 = j * TR;
-    if (!live || k0 > qw + 31) continue;
-    const unsigned char* Ks = sK + st * TILEB;
-    const unsigned char* Vs = sV + st * TILEB;
+    if (!live || k0 > qw + 31) return;
 
     f32x4 sc[2][4], dp[2][4];
 #pragma unroll
@@ -549,8 +601,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
     for (int stp = 0; stp < 4; ++stp)
 #pragma unroll
       for (int kf = 0; kf < 4; ++kf) {
-        const u32x4 kr = frag_rows(Ks, 16 * kf + s16, stp, g);
-        const u32x4 vr = frag_rows(Vs, 16 * kf + s16, stp, g);
+        const u32x4 kr = frag_rows<0>(lds + KO + 4096 * kf, roff[stp]);
+        const u32x4 vr = frag_rows<0>(lds + VO + 4096 * kf, roff[stp]);
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
           sc[f][kf] = mma(kr, qf[f][stp], sc[f][kf]);
@@ -558,20 +610,30 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
         }
       }
 
-    const bool diag = k0 + TR - 1 > qw;
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
       for (int kf = 0; kf < 4; ++kf)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float p = fexp2(fmaf(sc[f][kf][v], c, -lse2[f]));
-          if (diag && k0 + 16 * kf + 4 * g + v > qw + 16 * f + s16) p = 0.f;
-          sc[f][kf][v] = p * (dp[f][kf][v] - dsum[f]);  // dS
-        }
-
+        for (int v = 0; v < 4; ++v) sc[f][kf][v] = fexp2(fmaf(sc[f][kf][v], c, -lse2[f]));
+    if (k0 + TR - 1 > qw) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int kf = 0; kf < 4; ++kf)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (k0 + 16 * kf + 4 * g + v > qw + 16 * f + s16) sc[f][kf][v] = 0.f;
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int kf = 0; kf < 4; ++kf)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sc[f][kf][v] *= dp[f][kf][v] - dsum[f];  // dS
+
+    auto dqk = [&](auto tc) {
+      constexpr int t = decltype(tc)::value;
       u32x4 sb[2];
 #pragma unroll
       for (int f = 0; f < 2; ++f) sb[f] = pack_b(sc[f][2 * t], sc[f][2 * t + 1]);
@@ -579,14 +641,20 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
       for (int i0 = 0; i0 < 8; i0 += 2) {
         u32x4 kt[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) kt[u] = frag_cols(Ks, i0 + u, t, g, s16);
+        for (int u = 0; u < 2; ++u) kt[u] = frag_cols<KO + 8192 * t>(caddr[i0 + u]);
         lds_wait(kt);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int f = 0; f < 2; ++f) acc[f][i0 + u] = mma(kt[u], sb[f], acc[f][i0 + u]);
       }
-    }
+    };
+    dqk(IC<0>{});
+    dqk(IC<1>{});
+  };
+  for (int j = 0; j < nkt; j += 2) {
+    tile(IC<0>{}, j);
+    if (j + 1 < nkt) tile(IC<1>{}, j + 1);
   }
 
   if (!live) return;
@@ -611,11 +679,13 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Backward, dK and dV. Block: 128 keys of one (sequence, key/value head),
 // 4 waves of 32; for every query head of the group, query/dO tiles of 64
-// rows (with their LSE and D values) stream through two LDS stages, from the
-// tile holding the block's first key to the end of the sequence.
+// rows (with their LSE * log2(e) and D values) stream through two LDS
+// stages, from the tile holding the block's first key to the end of the
+// sequence. Each 64-query tile is taken in two halves of 32 queries, so the
+// score and dP accumulators of only one half are live at a time.
 // ---------------------------------------------------------------------------
 constexpr int KBN = 128;
-constexpr int KV_STAGE = 2 * TILEB + 2 * 256;  // Q, dO, LSE, D
+constexpr int KV_STAGE = 2 * TILEB + 2 * 256;  // Q, dO, LSE * log2(e), D
 constexpr int DKV_LDS = 2 * KV_STAGE;
 
 __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
@@ -633,7 +703,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   const int k0 = kt * KBN, kw = k0 + 32 * wave;
   const int qt0 = k0 / TR;
   const int nqt = (a.seq_len + TR - 1) / TR;
-  const int nit = grp * (nqt - qt0);  // (head, query tile) steps
+  const int nq = nqt - qt0;  // query tiles per head
+  const int nit = grp * nq;  // (head, query tile) steps
 
   const int64_t koff = tok0 * ldk + hk * DH;
   u32x4 kf[2][4], vf[2][4];
@@ -645,25 +716,31 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       vf[f][st] = load_row16(a.v + koff, ldk, kw + 16 * f + s16, a.seq_len, 32 * st + 8 * g);
     }
 
-  // Step it covers head h = hk * grp + it / (nqt - qt0), query tile
-  // qt0 + it % (nqt - qt0).
-  auto issue = [&](int it, unsigned char* stage) {
-    const int hq = hk * grp + it / (nqt - qt0);
-    const int qt = qt0 + it % (nqt - qt0);
-    const int64_t qoff = tok0 * ldq + (int64_t)hq * DH;
-    TileDma dq, dd;
-    dq.init(a.q + qoff, ldq, a.seq_len, lane, wave);
-    dd.init(a.dout + qoff, ldq, a.seq_len, lane, wave);
-    dq.issue(qt, stage, wave);
-    dd.issue(qt, stage + TILEB, wave);
-    if (wave == 0) {
-      RowDma r;
-      r.init(a.lse + (int64_t)hq * a.T + tok0, a.seq_len);
-      r.issue(qt, stage + 2 * TILEB, lane);
-    } else if (wave == 1) {
-      RowDma r;
-      r.init(a.dsum + (int64_t)hq * a.T + tok0, a.seq_len);
-      r.issue(qt, stage + 2 * TILEB + 256, lane);
+  uint32_t roff[4], caddr[8];
+  row_offsets(g, s16, roff);
+  col_offsets(g, s16, caddr);
+  const uint32_t lbase = lds_addr(lds);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) caddr[i] += lbase;
+
+  TileDma dq, dd;
+  dq.init(ldq, lane, wave);
+  dd.init(ldq, lane, wave);
+  // Next (head, query tile) to load.
+  int nh = hk * grp, nt = qt0;
+  auto issue = [&](unsigned char* stage) {
+    const int64_t qoff = tok0 * ldq + (int64_t)nh * DH;
+    dq.set(a.q + qoff, ldq, a.seq_len);
+    dd.set(a.dout + qoff, ldq, a.seq_len);
+    dq.issue(nt, stage, wave);
+    dd.issue(nt, stage + TILEB, wave);
+    if (wave == 0)
+      row_dma(a.lse2 + (int64_t)nh * a.T + tok0, a.seq_len, nt, stage + 2 * TILEB, lane);
+    else if (wave == 1)
+      row_dma(a.dsum + (int64_t)nh * a.T + tok0, a.seq_len, nt, stage + 2 * TILEB + 256, lane);
+    if (++nt == nqt) {
+      nt = qt0;
+      ++nh;
     }
   };
 
@@ -677,75 +754,86 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     }
   const float c = a.c;
   const bool live = kw < a.seq_len;
-  if (nit > 0) issue(0, lds);
+  if (nit > 0) issue(lds);
+  int cur_t = qt0;  // query tile of the current step
 
-  for (int it = 0; it < nit; ++it) {
-    const int st = it & 1;
-    unsigned char* stage = lds + st * KV_STAGE;
+  auto step = [&](auto stc, int it) {
+    constexpr int ST = decltype(stc)::value;
+    constexpr int QO = ST * KV_STAGE, DO = QO + TILEB, LO = QO + 2 * TILEB, SO = LO + 256;
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     block_barrier();
-    if (it + 1 < nit) issue(it + 1, lds + (st ^ 1) * KV_STAGE);
-    const int qs = (qt0 + it % (nqt - qt0)) * TR;
-    if (!live || qs + TR - 1 < kw) continue;  // every query before every key of this wave
-    const unsigned char* Qs = stage;
-    const unsigned char* Ds = stage + TILEB;
-    const float* lrow = reinterpret_cast<const float*>(stage + 2 * TILEB);
-    const float* drow = reinterpret_cast<const float*>(stage + 2 * TILEB + 256);
+    if (it + 1 < nit) issue(lds + (ST ^ 1) * KV_STAGE);
+    const int qs = cur_t * TR;
+    if (++cur_t == nqt) cur_t = qt0;
+    if (!live || qs + TR - 1 < kw) return;  // every query before every key of this wave
+    const float* lrow = reinterpret_cast<const float*>(lds + LO);
+    const float* drow = reinterpret_cast<const float*>(lds + SO);
 
-    f32x4 sc[2][4], dp[2][4];
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int qf = 0; qf < 4; ++qf) {
-        sc[f][qf] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[f][qf] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-    for (int stp = 0; stp < 4; ++stp)
-#pragma unroll
-      for (int qf = 0; qf < 4; ++qf) {
-        const u32x4 qr = frag_rows(Qs, 16 * qf + s16, stp, g);
-        const u32x4 dr = frag_rows(Ds, 16 * qf + s16, stp, g);
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          sc[f][qf] = mma(qr, kf[f][stp], sc[f][qf]);
-          dp[f][qf] = mma(dr, vf[f][stp], dp[f][qf]);
-        }
-      }
-
-    const bool diag = qs < kw + 31;  // some query before some key of this wave
-    f32x4 pp[2][4];
-#pragma unroll
-    for (int qf = 0; qf < 4; ++qf) {
-      const f32x4 lv = *reinterpret_cast<const f32x4*>(lrow + 16 * qf + 4 * g);
-      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(drow + 16 * qf + 4 * g);
+    auto half = [&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      f32x4 sc[2][2], dp[2][2];
 #pragma unroll
       for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float p = fexp2(fmaf(sc[f][qf][v], c, -lv[v] * kLog2e));
-          if (diag && kw + 16 * f + s16 > qs + 16 * qf + 4 * g + v) p = 0.f;
-          pp[f][qf][v] = p;
-          sc[f][qf][v] = p * (dp[f][qf][v] - dv4[v]);  // dS
+        for (int qq = 0; qq < 2; ++qq) {
+          sc[f][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[f][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    }
-
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int stp = 0; stp < 4; ++stp)
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          const int qf = 2 * t + qq;
+          const u32x4 qr = frag_rows<0>(lds + QO + 4096 * qf, roff[stp]);
+          const u32x4 dr = frag_rows<0>(lds + DO + 4096 * qf, roff[stp]);
+#pragma unroll
+          for (int f = 0; f < 2; ++f) {
+            sc[f][qq] = mma(qr, kf[f][stp], sc[f][qq]);
+            dp[f][qq] = mma(dr, vf[f][stp], dp[f][qq]);
+          }
+        }
+
+      const int qb = qs + 32 * t;  // first query of this half
+      f32x4 lv[2], dv4[2];
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        lv[qq] = *reinterpret_cast<const f32x4*>(lrow + 32 * t + 16 * qq + 4 * g);
+        dv4[qq] = *reinterpret_cast<const f32x4*>(drow + 32 * t + 16 * qq + 4 * g);
+      }
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sc[f][qq][v] = fexp2(fmaf(sc[f][qq][v], c, -lv[qq][v]));
+      if (qb < kw + 31) {  // some query of this half before some key of this wave
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (kw + 16 * f + s16 > qb + 16 * qq + 4 * g + v) sc[f][qq][v] = 0.f;
+      }
       u32x4 pb[2], sb[2];
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
-        pb[f] = pack_b(pp[f][2 * t], pp[f][2 * t + 1]);
-        sb[f] = pack_b(sc[f][2 * t], sc[f][2 * t + 1]);
+        pb[f] = pack_b(sc[f][0], sc[f][1]);
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sc[f][qq][v] *= dp[f][qq][v] - dv4[qq][v];  // dS
+        sb[f] = pack_b(sc[f][0], sc[f][1]);
       }
+
 #pragma unroll
       for (int i0 = 0; i0 < 8; i0 += 2) {
-        u32x4 fr[4];  // dO^T and Q^T fragments of columns i0, i0 + 1
+        u32x4 fr[4];  // dO^T and Q^T fragments of column blocks i0, i0 + 1
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          fr[2 * u] = frag_cols(Ds, i0 + u, t, g, s16);
-          fr[2 * u + 1] = frag_cols(Qs, i0 + u, t, g, s16);
+          fr[2 * u] = frag_cols<DO + 8192 * t>(caddr[i0 + u]);
+          fr[2 * u + 1] = frag_cols<QO + 8192 * t>(caddr[i0 + u]);
         }
         lds_wait(fr);
 #pragma unroll
@@ -756,7 +844,13 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
             dka[f][i0 + u] = mma(fr[2 * u + 1], sb[f], dka[f][i0 + u]);
           }
       }
-    }
+    };
+    half(IC<0>{});
+    half(IC<1>{});
+  };
+  for (int it = 0; it < nit; it += 2) {
+    step(IC<0>{}, it);
+    if (it + 1 < nit) step(IC<1>{}, it + 1);
   }
 
   if (!live) return;
@@ -822,6 +916,7 @@ static BwdArgs bwd_args(const AttnDesc& d) {
   a.dout = static_cast<const bf16_t*>(d.dout);
   a.lse = d.lse;
   a.dsum = d.dsum;
+  a.lse2 = d.lse2;
   a.dq = static_cast<bf16_t*>(d.dq);
   a.dk = static_cast<bf16_t*>(d.dk);
   a.dv = static_cast<bf16_t*>(d.dv);

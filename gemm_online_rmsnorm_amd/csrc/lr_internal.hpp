@@ -98,6 +98,7 @@ struct AttnDesc {
   const void* dout = nullptr;
   float* lse = nullptr;
   float* dsum = nullptr;
+  float* lse2 = nullptr;
   void* dq = nullptr;
   void* dk = nullptr;
   void* dv = nullptr;
@@ -105,7 +106,7 @@ struct AttnDesc {
 hipError_t run_rope(const void* x, void* y, int T, int heads, int seq_len, double rope_base,
                     bool inverse, hipStream_t s);
 hipError_t run_attn_fwd(const AttnDesc& d, hipStream_t s);
-hipError_t run_attn_dq(const AttnDesc& d, hipStream_t s);    // also writes d.dsum
-hipError_t run_attn_dkdv(const AttnDesc& d, hipStream_t s);  // reads d.dsum
+hipError_t run_attn_dq(const AttnDesc& d, hipStream_t s);    // also writes d.dsum, d.lse2
+hipError_t run_attn_dkdv(const AttnDesc& d, hipStream_t s);  // reads d.dsum, d.lse2
 
 }  // namespace lr
