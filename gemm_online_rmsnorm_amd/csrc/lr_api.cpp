@@ -17,6 +17,7 @@
 
 #include "../../include/lr_block.h"
 #include "lr_internal.hpp"
+#include "lr_attn.hpp"
 
 namespace {
 

@@ -32,11 +32,10 @@
 // apart).
 //
 // Key/value (or query/dO) tiles of 64 rows x 256 bytes go from HBM to LDS
-// with buffer_load_dwordx4 ... lds, double-buffered; the 16-byte chunk c of
-// tile row r is stored at chunk c ^ (r & 15), which keeps both the 16-byte
-// fragment reads (16 rows, one chunk) and the transposing reads (16 rows,
-// 32 bytes each) spread over the banks. Rows past the end of a sequence lie
-// outside the buffer range and read as zeros.
+// with buffer_load_dwordx4 ... lds, double-buffered, their 16-byte chunks
+// XOR-swizzled by row (swz below) so that both fragment reads are free of
+// bank conflicts. Rows past the end of a sequence lie outside the buffer
+// range and read as zeros.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -46,6 +45,7 @@
 #include "lr_common.hpp"
 #include "lr_gemm2.hpp"
 #include "lr_internal.hpp"
+#include "lr_attn.hpp"
 
 namespace lr {
 namespace {
@@ -109,12 +109,12 @@ __device__ __forceinline__ int xcd_item(int nwg) {
 }
 
 // 16-byte chunk c of row r of a streamed tile sits at chunk c ^ swz(r).
-// The sixteen rows of a 16-byte fragment read (rows r0 .. r0 + 15, one
-// logical chunk) land on sixteen distinct chunks, and so do the sixteen
-// (row, chunk) pairs each half-wave of a transposing read touches (rows
-// r0 + 0..7 or r0 + 8..15, chunks 2i and 2i + 1): both reads are free of
-// bank conflicts.
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// Measured with the LDS bank-conflict counter on this hardware: with
+// 2 (r & 7) both the 16-byte row-fragment reads (16 rows, one logical
+// chunk per lane group) and the transposing reads (rows 4g + s/4, 32 bytes
+// each) are conflict-free; c ^ (r & 15) leaves the transposing reads 2-way
+// conflicted and c ^ (2 (r & 7) + (r >> 3)) the 16-byte reads.
+__device__ __forceinline__ int swz(int r) { return 2 * (r & 7); }
 
 // HBM-to-LDS copy of 64-row tiles of a [rows][128] bf16 head slice with
 // row stride ld: 16 blocks of 1 KB (4 rows each), four per wave. The
@@ -377,96 +377,133 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   float m[2] = {kMasked, kMasked}, l[2] = {0.f, 0.f};
   const float c = a.c;
   const bool live = qw < a.seq_len;
+  // Tile j holds a key at or before this wave's last query.
+  auto needed = [&](int j) { return live && j * TR <= qw + 31; };
 
-  auto tile = [&](auto stc, int j) {
-    constexpr int ST = decltype(stc)::value;
-    constexpr int KO = ST * TILEB, VO = 2 * TILEB + ST * TILEB;
-    wait_vmcnt<0>();
-    wait_lgkmcnt0();
-    block_barrier();
-    if (j + 1 < nkt) {
-      dk.issue(j + 1, lds + (ST ^ 1) * TILEB, wave);
-      dv.issue(j + 1, lds + 2 * TILEB + (ST ^ 1) * TILEB, wave);
-    }
-    const int k0 = j * TR;
-    if (!live || k0 > qw + 31) return;  // every key after every query of this wave
-
-    f32x4 sc[2][4];
+  // Scores of a key tile from the K stage at byte offset KO.
+  auto scores = [&](auto koc, f32x4 (&s)[2][4]) {
+    constexpr int KO = decltype(koc)::value;
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int kf = 0; kf < 4; ++kf) sc[f][kf] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kf = 0; kf < 4; ++kf) s[f][kf] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int stp = 0; stp < 4; ++stp)
 #pragma unroll
       for (int kf = 0; kf < 4; ++kf) {
         const u32x4 kr = frag_rows<0>(lds + KO + 4096 * kf, roff[stp]);
 #pragma unroll
-        for (int f = 0; f < 2; ++f) sc[f][kf] = mma(kr, qf[f][stp], sc[f][kf]);
+        for (int f = 0; f < 2; ++f) s[f][kf] = mma(kr, qf[f][stp], s[f][kf]);
       }
-
-    if (k0 + TR - 1 > qw) {  // the tile crosses this wave's diagonal
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int kf = 0; kf < 4; ++kf)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (k0 + 16 * kf + 4 * g + v > qw + 16 * f + s16) sc[f][kf][v] = kMasked;
-    }
-
+  };
+  // Online softmax of one tile's scores: raises the running maximum when
+  // needed (alpha: the factor O and the row sum are rescaled by), adds the
+  // probabilities to the row sums and packs them as B operands.
+  auto softmax = [&](f32x4 (&s)[2][4], float (&alpha)[2], u32x4 (&pb)[2][2]) {
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
       float mx = m[f];
 #pragma unroll
       for (int kf = 0; kf < 4; ++kf)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, sc[f][kf][v]);
+        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[f][kf][v]);
       mx = xg_max(mx);
       const bool grow = (mx - m[f]) * c > kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float alpha = grow ? fexp2((m[f] - mx) * c) : 1.0f;
-        m[f] = grow ? mx : m[f];
-        l[f] *= alpha;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[f][i] *= alpha;
-      }
+      alpha[f] = grow ? fexp2((m[f] - mx) * c) : 1.0f;
+      m[f] = grow ? mx : m[f];
       const float mc = m[f] * c;
       float rs = 0.f;
 #pragma unroll
       for (int kf = 0; kf < 4; ++kf)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float p = fexp2(fmaf(sc[f][kf][v], c, -mc));
-          sc[f][kf][v] = p;
+          const float p = fexp2(fmaf(s[f][kf][v], c, -mc));
+          s[f][kf][v] = p;
           rs += p;
         }
-      l[f] += rs;
-    }
-
-    auto pv = [&](auto tc) {
-      constexpr int t = decltype(tc)::value;
-      u32x4 pb[2];
+      l[f] = l[f] * alpha[f] + rs;
 #pragma unroll
-      for (int f = 0; f < 2; ++f) pb[f] = pack_b(sc[f][2 * t], sc[f][2 * t + 1]);
+      for (int t = 0; t < 2; ++t) pb[t][f] = pack_b(s[f][2 * t], s[f][2 * t + 1]);
+    }
+  };
+
+  f32x4 sA[2][4], sB[2][4];
+  if (nkt > 1) dk.issue(1, lds + TILEB, wave);
+  wait_vmcnt<0>();
+  block_barrier();
+  if (needed(0)) scores(IC<0>{}, sA);
+
+  // Step j: scores of tile j are in sc; K of tile j + 1 and V of tile j
+  // are in LDS. Loads K of tile j + 2 and V of tile j + 1, forms the scores
+  // of tile j + 1 (overlapping this tile's softmax) and adds P V.
+  auto tile = [&](auto stc, int j, f32x4 (&sc)[2][4], f32x4 (&sn)[2][4]) {
+    constexpr int ST = decltype(stc)::value;
+    constexpr int KN = (ST ^ 1) * TILEB;        // K stage of tile j + 1
+    constexpr int VO = 2 * TILEB + ST * TILEB;  // V stage of tile j
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    block_barrier();
+    if (j + 2 < nkt) dk.issue(j + 2, lds + ST * TILEB, wave);
+    if (j + 1 < nkt) dv.issue(j + 1, lds + 2 * TILEB + (ST ^ 1) * TILEB, wave);
+    if (!needed(j)) return;
+    const int k0 = j * TR;
+    const bool next = j + 1 < nkt && needed(j + 1);
+    float alpha[2];
+    u32x4 pb[2][2];
+    if (k0 + TR - 1 > qw || !next) {  // a tile on the diagonal, or the last one
+      if (k0 + TR - 1 > qw) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int kf = 0; kf < 4; ++kf)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (k0 + 16 * kf + 4 * g + v > qw + 16 * f + s16) sc[f][kf][v] = kMasked;
+      }
+      softmax(sc, alpha, pb);
+      if (next) scores(IC<KN>{}, sn);
+    } else {
+      scores(IC<KN>{}, sn);
+      softmax(sc, alpha, pb);
+      // Interleave: the score products of the next tile run on the matrix
+      // cores while this tile's softmax runs on the vector ALUs.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
+        if (k < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[f][i] *= alpha[f];
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int i0 = 0; i0 < 8; i0 += 4) {
         u32x4 vt[4];
+        if (t == 0) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) vt[u] = frag_cols<VO + 8192 * t>(caddr[i0 + u]);
+          for (int u = 0; u < 4; ++u) vt[u] = frag_cols<VO>(caddr[i0 + u]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) vt[u] = frag_cols<VO + 8192>(caddr[i0 + u]);
+        }
         lds_wait(vt);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int f = 0; f < 2; ++f) o[f][i0 + u] = mma(vt[u], pb[f], o[f][i0 + u]);
+          for (int f = 0; f < 2; ++f) o[f][i0 + u] = mma(vt[u], pb[t][f], o[f][i0 + u]);
       }
-    };
-    pv(IC<0>{});
-    pv(IC<1>{});
+    }
   };
   for (int j = 0; j < nkt; j += 2) {
-    tile(IC<0>{}, j);
-    if (j + 1 < nkt) tile(IC<1>{}, j + 1);
+    tile(IC<0>{}, j, sA, sB);
+    if (j + 1 < nkt) tile(IC<1>{}, j + 1, sB, sA);
   }
 
   if (!live) return;

@@ -30,11 +30,17 @@ CSRC = os.path.join(HERE, "csrc")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
+# Sources of the block's GEMM and memory-bound kernels and their launch
+# code (the attention kernels and the C ABI layer are built from other files).
+KERNEL_SOURCES = ("lr_kernels.hip", "lr_common.hpp", "lr_gemm.hpp", "lr_gemm2.hpp",
+                  "lr_internal.hpp")
+
+
 def source_hash() -> str:
-    """SHA-256 over the HIP/C++ sources the kernels are built from."""
+    """SHA-256 over the sources the block's kernels are built from."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+        if name in KERNEL_SOURCES:
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
