@@ -369,12 +369,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     for (int st = 0; st < 4; ++st)
       qf[f][st] = load_row16(qbase, ldq, qw + 16 * f + s16, a.seq_len, 32 * st + 8 * g);
 
-  f32x4 o[2][8];
+  // o[f][8] accumulates the row sums of P: its A operand is a block whose
+  // row 0 is all ones, so row 0 of the result (lanes of group 0, element 0)
+  // is the sum over the tile's keys, and rescaling it with O keeps it
+  // consistent.
+  f32x4 o[2][9];
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {kMasked, kMasked}, l[2] = {0.f, 0.f};
+    for (int i = 0; i < 9; ++i) o[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t one2 = s16 == 0 ? 0x3F803F80u : 0u;  // two bf16 ones in row 0
+  const u32x4 ones = {one2, one2, one2, one2};
+  float m[2] = {kMasked, kMasked};
   const float c = a.c;
   const bool live = qw < a.seq_len;
   // Tile j holds a key at or before this wave's last query.
@@ -397,8 +403,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
       }
   };
   // Online softmax of one tile's scores: raises the running maximum when
-  // needed (alpha: the factor O and the row sum are rescaled by), adds the
-  // probabilities to the row sums and packs them as B operands.
+  // needed (alpha: the factor O and the row sums are rescaled by) and packs
+  // the probabilities as B operands.
   auto softmax = [&](f32x4 (&s)[2][4], float (&alpha)[2], u32x4 (&pb)[2][2]) {
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
@@ -412,77 +418,53 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
       alpha[f] = grow ? fexp2((m[f] - mx) * c) : 1.0f;
       m[f] = grow ? mx : m[f];
       const float mc = m[f] * c;
-      float rs = 0.f;
 #pragma unroll
       for (int kf = 0; kf < 4; ++kf)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float p = fexp2(fmaf(s[f][kf][v], c, -mc));
-          s[f][kf][v] = p;
-          rs += p;
-        }
-      l[f] = l[f] * alpha[f] + rs;
+        for (int v = 0; v < 4; ++v) s[f][kf][v] = fexp2(fmaf(s[f][kf][v], c, -mc));
 #pragma unroll
       for (int t = 0; t < 2; ++t) pb[t][f] = pack_b(s[f][2 * t], s[f][2 * t + 1]);
     }
   };
 
-  f32x4 sA[2][4], sB[2][4];
-  if (nkt > 1) dk.issue(1, lds + TILEB, wave);
-  wait_vmcnt<0>();
-  block_barrier();
-  if (needed(0)) scores(IC<0>{}, sA);
-
-  // Step j: scores of tile j are in sc; K of tile j + 1 and V of tile j
-  // are in LDS. Loads K of tile j + 2 and V of tile j + 1, forms the scores
-  // of tile j + 1 (overlapping this tile's softmax) and adds P V.
-  auto tile = [&](auto stc, int j, f32x4 (&sc)[2][4], f32x4 (&sn)[2][4]) {
+  // Step j: K and V of tile j are in LDS stage j & 1; loads tile j + 1
+  // into the other stage, then scores, softmax and P V.
+  auto tile = [&](auto stc, int j) {
     constexpr int ST = decltype(stc)::value;
-    constexpr int KN = (ST ^ 1) * TILEB;        // K stage of tile j + 1
-    constexpr int VO = 2 * TILEB + ST * TILEB;  // V stage of tile j
+    constexpr int KO = ST * TILEB, VO = 2 * TILEB + ST * TILEB;
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     block_barrier();
-    if (j + 2 < nkt) dk.issue(j + 2, lds + ST * TILEB, wave);
-    if (j + 1 < nkt) dv.issue(j + 1, lds + 2 * TILEB + (ST ^ 1) * TILEB, wave);
+    if (j + 1 < nkt) {
+      dk.issue(j + 1, lds + (ST ^ 1) * TILEB, wave);
+      dv.issue(j + 1, lds + 2 * TILEB + (ST ^ 1) * TILEB, wave);
+    }
     if (!needed(j)) return;
     const int k0 = j * TR;
-    const bool next = j + 1 < nkt && needed(j + 1);
+    f32x4 sc[2][4];
+    scores(IC<KO>{}, sc);
+    if (k0 + TR - 1 > qw) {  // the tile crosses this wave's diagonal
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int kf = 0; kf < 4; ++kf)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (k0 + 16 * kf + 4 * g + v > qw + 16 * f + s16) sc[f][kf][v] = kMasked;
+    }
     float alpha[2];
     u32x4 pb[2][2];
-    if (k0 + TR - 1 > qw || !next) {  // a tile on the diagonal, or the last one
-      if (k0 + TR - 1 > qw) {
-#pragma unroll
-        for (int f = 0; f < 2; ++f)
-#pragma unroll
-          for (int kf = 0; kf < 4; ++kf)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (k0 + 16 * kf + 4 * g + v > qw + 16 * f + s16) sc[f][kf][v] = kMasked;
-      }
-      softmax(sc, alpha, pb);
-      if (next) scores(IC<KN>{}, sn);
-    } else {
-      scores(IC<KN>{}, sn);
-      softmax(sc, alpha, pb);
-      // Interleave: the score products of the next tile run on the matrix
-      // cores while this tile's softmax runs on the vector ALUs.
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
-        if (k < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
+    softmax(sc, alpha, pb);
     if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
 #pragma unroll
       for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[f][i] *= alpha[f];
+        for (int i = 0; i < 9; ++i) o[f][i] *= alpha[f];
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) o[f][8] = mma(ones, pb[t][f], o[f][8]);
 #pragma unroll
       for (int i0 = 0; i0 < 8; i0 += 4) {
         u32x4 vt[4];
@@ -502,8 +484,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     }
   };
   for (int j = 0; j < nkt; j += 2) {
-    tile(IC<0>{}, j, sA, sB);
-    if (j + 1 < nkt) tile(IC<1>{}, j + 1, sB, sA);
+    tile(IC<0>{}, j);
+    if (j + 1 < nkt) tile(IC<1>{}, j + 1);
   }
 
   if (!live) return;
@@ -511,7 +493,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     const int row = qw + 16 * f + s16;
-    const float lt = xg_sum(l[f]);
+    const float lt = xg_sum(o[f][8][0]);  // only group 0 holds row 0 of the sums
     if (row >= a.seq_len) continue;
     const float inv = 1.0f / lt;
 #pragma unroll
