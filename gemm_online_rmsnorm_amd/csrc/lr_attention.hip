@@ -117,19 +117,21 @@ __device__ __forceinline__ int xcd_item(int nwg) {
 __device__ __forceinline__ int swz(int r) { return 2 * (r & 7); }
 
 // HBM-to-LDS copy of 64-row tiles of a [rows][128] bf16 head slice with
-// row stride ld: 16 blocks of 1 KB (4 rows each), four per wave. The
+// row stride ld: 16 blocks of 1 KB (4 rows each), shared by NW waves. The
 // per-lane offsets depend only on ld; the buffer resource (base and the
 // slice's extent, so rows past the end read zeros) is set per slice.
-struct TileDma {
+template <int NW>
+struct TileDmaT {
+  static constexpr int PER = 16 / NW;  // 1 KB blocks per wave
 #if defined(__HIP_DEVICE_COMPILE__)
   __amdgpu_buffer_rsrc_t rs;
 #endif
-  uint32_t off[4];
+  uint32_t off[PER];
   uint32_t step;  // bytes between consecutive tiles
   __device__ __forceinline__ void init(int64_t ld, int lane, int wave) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int blk = 4 * v + wave;
+    for (int v = 0; v < PER; ++v) {
+      const int blk = NW * v + wave;
       const int r = 4 * blk + (lane >> 4);
       const int c = (lane & 15) ^ swz(r);
       off[v] = (uint32_t)(2 * ((int64_t)r * ld + 8 * c));
@@ -148,14 +150,16 @@ struct TileDma {
   __device__ __forceinline__ void issue(int tile, unsigned char* dst, int wave) const {
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LR_LPTR(dst + (4 * v + wave) * 1024), 16,
+    for (int v = 0; v < PER; ++v)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LR_LPTR(dst + (NW * v + wave) * 1024), 16,
                                                off[v] + (uint32_t)tile * step, 0, 0, 0);
 #else
     (void)tile; (void)dst; (void)wave;
 #endif
   }
 };
+
+using TileDma = TileDmaT<4>;
 
 // HBM-to-LDS copy of 64 consecutive fp32 values (one per row of a tile),
 // issued by one wave; values past `n` read as zeros.
@@ -218,6 +222,15 @@ __device__ __forceinline__ void lds_wait(u32x4 (&x)[4]) {
 }
 __device__ __forceinline__ void lds_wait(u32x4 (&x)[2]) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1])::"memory");
+}
+// The same, leaving the N most recent LDS reads in flight (LDS reads
+// return in order, so the older group's fragments have arrived).
+template <int N>
+__device__ __forceinline__ void lds_wait_keep(u32x4 (&x)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)"
+               : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])
+               : "n"(N)
+               : "memory");
 }
 
 // B operand of k-step t from score blocks 2t and 2t + 1 of one row set.
@@ -461,27 +474,36 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 9; ++i) o[f][i] *= alpha[f];
     }
+    // V^T fragments of four column blocks per group, two buffers: the next
+    // group's reads are in flight while this group's products run.
+    auto load = [&](auto tc, u32x4 (&vt)[4], int i0) {
+      constexpr int t = decltype(tc)::value;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int u = 0; u < 4; ++u) vt[u] = frag_cols<VO + 8192 * t>(caddr[i0 + u]);
+    };
+    auto pv = [&](int t, u32x4 (&vt)[4], int i0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int f = 0; f < 2; ++f) o[f][i0 + u] = mma(vt[u], pb[t][f], o[f][i0 + u]);
+    };
+    u32x4 va[4], vb[4];
+    load(IC<0>{}, va, 0);
+    load(IC<0>{}, vb, 4);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int f = 0; f < 2; ++f) o[f][8] = mma(ones, pb[t][f], o[f][8]);
-#pragma unroll
-      for (int i0 = 0; i0 < 8; i0 += 4) {
-        u32x4 vt[4];
-        if (t == 0) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) vt[u] = frag_cols<VO>(caddr[i0 + u]);
-        } else {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) vt[u] = frag_cols<VO + 8192>(caddr[i0 + u]);
-        }
-        lds_wait(vt);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int f = 0; f < 2; ++f) o[f][i0 + u] = mma(vt[u], pb[t][f], o[f][i0 + u]);
-      }
-    }
+    lds_wait_keep<8>(va);
+    pv(0, va, 0);
+    load(IC<1>{}, va, 0);
+    lds_wait_keep<8>(vb);
+    pv(0, vb, 4);
+    load(IC<1>{}, vb, 4);
+    lds_wait_keep<8>(va);
+    pv(1, va, 0);
+    lds_wait_keep<0>(vb);
+    pv(1, vb, 4);
   };
   for (int j = 0; j < nkt; j += 2) {
     tile(IC<0>{}, j);
@@ -706,8 +728,12 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
 constexpr int KBN = 128;
 constexpr int KV_STAGE = 2 * TILEB + 2 * 256;  // Q, dO, LSE * log2(e), D
 constexpr int DKV_LDS = 2 * KV_STAGE;
+constexpr int kDkdvWaves = 8;  // 8 waves of 16 keys (2 per SIMD) or 4 of 32
 
-__global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
+template <int NWK>
+__global__ __launch_bounds__(64 * NWK, 1) void attn_dkdv_kernel(BwdArgs a) {
+  constexpr int FK = KBN / (16 * NWK);  // 16-key fragments per wave
+  constexpr int KPW = 16 * FK;          // keys per wave
   extern __shared__ __align__(16) unsigned char lds[];
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
@@ -719,16 +745,16 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   const int grp = a.H / a.Hkv;
   const int64_t ldq = (int64_t)a.H * DH, ldk = (int64_t)a.Hkv * DH;
   const int64_t tok0 = (int64_t)b * a.seq_len;
-  const int k0 = kt * KBN, kw = k0 + 32 * wave;
+  const int k0 = kt * KBN, kw = k0 + KPW * wave;
   const int qt0 = k0 / TR;
   const int nqt = (a.seq_len + TR - 1) / TR;
   const int nq = nqt - qt0;  // query tiles per head
   const int nit = grp * nq;  // (head, query tile) steps
 
   const int64_t koff = tok0 * ldk + hk * DH;
-  u32x4 kf[2][4], vf[2][4];
+  u32x4 kf[FK][4], vf[FK][4];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int f = 0; f < FK; ++f)
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       kf[f][st] = load_row16(a.k + koff, ldk, kw + 16 * f + s16, a.seq_len, 32 * st + 8 * g);
@@ -742,7 +768,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) caddr[i] += lbase;
 
-  TileDma dq, dd;
+  TileDmaT<NWK> dq, dd;
   dq.init(ldq, lane, wave);
   dd.init(ldq, lane, wave);
   // Next (head, query tile) to load.
@@ -763,9 +789,9 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  f32x4 dka[2][8], dva[2][8];
+  f32x4 dka[FK][8], dva[FK][8];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int f = 0; f < FK; ++f)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       dka[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -789,11 +815,11 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     const float* lrow = reinterpret_cast<const float*>(lds + LO);
     const float* drow = reinterpret_cast<const float*>(lds + SO);
 
-    auto half = [&](auto tc) {
+    // Scores and dP of query half t (queries qs + 32t .. + 31).
+    auto sdp = [&](auto tc, f32x4 (&sc)[FK][2], f32x4 (&dp)[FK][2]) {
       constexpr int t = decltype(tc)::value;
-      f32x4 sc[2][2], dp[2][2];
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+      for (int f = 0; f < FK; ++f)
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
           sc[f][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -807,13 +833,18 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
           const u32x4 qr = frag_rows<0>(lds + QO + 4096 * qf, roff[stp]);
           const u32x4 dr = frag_rows<0>(lds + DO + 4096 * qf, roff[stp]);
 #pragma unroll
-          for (int f = 0; f < 2; ++f) {
+          for (int f = 0; f < FK; ++f) {
             sc[f][qq] = mma(qr, kf[f][stp], sc[f][qq]);
             dp[f][qq] = mma(dr, vf[f][stp], dp[f][qq]);
           }
         }
-
-      const int qb = qs + 32 * t;  // first query of this half
+    };
+    // P and dS of half t, packed as B operands; masked when the half
+    // crosses this wave's diagonal.
+    auto soft = [&](auto tc, f32x4 (&sc)[FK][2], const f32x4 (&dp)[FK][2],
+                    u32x4 (&pb)[FK], u32x4 (&sb)[FK], bool diag) {
+      constexpr int t = decltype(tc)::value;
+      const int qb = qs + 32 * t;
       f32x4 lv[2], dv4[2];
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
@@ -821,23 +852,22 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
         dv4[qq] = *reinterpret_cast<const f32x4*>(drow + 32 * t + 16 * qq + 4 * g);
       }
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+      for (int f = 0; f < FK; ++f)
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
           for (int v = 0; v < 4; ++v) sc[f][qq][v] = fexp2(fmaf(sc[f][qq][v], c, -lv[qq][v]));
-      if (qb < kw + 31) {  // some query of this half before some key of this wave
+      if (diag) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+        for (int f = 0; f < FK; ++f)
 #pragma unroll
           for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
               if (kw + 16 * f + s16 > qb + 16 * qq + 4 * g + v) sc[f][qq][v] = 0.f;
       }
-      u32x4 pb[2], sb[2];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
+      for (int f = 0; f < FK; ++f) {
         pb[f] = pack_b(sc[f][0], sc[f][1]);
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq)
@@ -845,24 +875,50 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
           for (int v = 0; v < 4; ++v) sc[f][qq][v] *= dp[f][qq][v] - dv4[qq][v];  // dS
         sb[f] = pack_b(sc[f][0], sc[f][1]);
       }
-
-#pragma unroll
-      for (int i0 = 0; i0 < 8; i0 += 2) {
-        u32x4 fr[4];  // dO^T and Q^T fragments of column blocks i0, i0 + 1
+    };
+    // dV += P^T dO and dK += dS^T Q for half t. dO^T and Q^T fragments of
+    // column blocks i0, i0 + 1 go through two buffers: the reads of the
+    // next pair are in flight while this pair's products run.
+    auto grads = [&](auto tc, const u32x4 (&pb)[FK], const u32x4 (&sb)[FK]) {
+      constexpr int t = decltype(tc)::value;
+      auto load = [&](u32x4 (&fr)[4], int i0) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           fr[2 * u] = frag_cols<DO + 8192 * t>(caddr[i0 + u]);
           fr[2 * u + 1] = frag_cols<QO + 8192 * t>(caddr[i0 + u]);
         }
-        lds_wait(fr);
+      };
+      auto prod = [&](u32x4 (&fr)[4], int i0) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int f = 0; f < 2; ++f) {
+          for (int f = 0; f < FK; ++f) {
             dva[f][i0 + u] = mma(fr[2 * u], pb[f], dva[f][i0 + u]);
             dka[f][i0 + u] = mma(fr[2 * u + 1], sb[f], dka[f][i0 + u]);
           }
-      }
+      };
+      u32x4 fa[4], fb[4];
+      load(fa, 0);
+      load(fb, 2);
+      lds_wait_keep<8>(fa);
+      prod(fa, 0);
+      load(fa, 4);
+      lds_wait_keep<8>(fb);
+      prod(fb, 2);
+      load(fb, 6);
+      lds_wait_keep<8>(fa);
+      prod(fa, 4);
+      lds_wait_keep<0>(fb);
+      prod(fb, 6);
+    };
+
+    auto half = [&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      f32x4 sc[FK][2], dp[FK][2];
+      u32x4 pb[FK], sb[FK];
+      sdp(tc, sc, dp);
+      soft(tc, sc, dp, pb, sb, qs + 32 * t < kw + KPW - 1);
+      grads(tc, pb, sb);
     };
     half(IC<0>{});
     half(IC<1>{});
@@ -879,7 +935,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) tpp[i][v] = rope_tpp(16 * i + 4 * g + v, a.log2_base);
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int f = 0; f < FK; ++f) {
     const int row = kw + 16 * f + s16;
     if (row >= a.seq_len) continue;
     rope_inverse_acc(dka[f], tpp, row, a.scale);
@@ -961,14 +1017,15 @@ hipError_t run_attn_dkdv(const AttnDesc& d, hipStream_t s) {
   BwdArgs a = bwd_args(d);
   a.ntiles = (d.seq_len + KBN - 1) / KBN;
   a.nbh = (d.T / d.seq_len) * d.Hkv;
+  auto kern = &attn_dkdv_kernel<kDkdvWaves>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_dkdv_kernel),
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, DKV_LDS);
   });
   if (attr_err != hipSuccess) return attr_err;
-  hipLaunchKernelGGL(attn_dkdv_kernel, dim3(a.ntiles * a.nbh), dim3(256), DKV_LDS, s, a);
+  hipLaunchKernelGGL(kern, dim3(a.ntiles * a.nbh), dim3(64 * kDkdvWaves), DKV_LDS, s, a);
   return hipGetLastError();
 }
 
