@@ -191,19 +191,17 @@ def attention_main(args):
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import attention as oa
-        S, nh = s.seq_len, 2
-        grp = s.H // s.Hkv
-        sl = {n: inp[n][:S, :nh * s.dh] for n in ("Q", "dO")}
-        kv = {n: inp[n][:S, :s.dh] for n in ("K", "V")}
+        S = s.seq_len  # the first sequence, every head
+        sl = {n: inp[n][:S] for n in ("Q", "K", "V", "dO")}
         t0 = time.perf_counter()
-        oa.attention_forward(sl["Q"], kv["K"], kv["V"], S, nh, 1, s.dh, s.base)
-        oa.attention_backward(sl["Q"], kv["K"], kv["V"], sl["dO"], S, nh, 1, s.dh, s.base)
+        oa.attention_forward(sl["Q"], sl["K"], sl["V"], S, s.H, s.Hkv, s.dh, s.base)
+        oa.attention_backward(sl["Q"], sl["K"], sl["V"], sl["dO"], S, s.H, s.Hkv, s.dh, s.base)
         dt = time.perf_counter() - t0
-        cfl = 14 * s.dh * (S * (S + 1) / 2) * nh
+        cfl = 14 * s.dh * (S * (S + 1) / 2) * s.H
         cpu = {"value": round(cfl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": _blas_threads(),
                "kind": "oracle", "seconds": round(dt, 2),
-               "sample": f"one sequence of {S} tokens, {nh} query heads sharing one "
-                         f"key/value head (grp {grp} in the workload), fwd+bwd, numpy float64"}
+               "sample": f"the first of {s.n_seq} sequences ({S} tokens), all {s.H} query heads "
+                         f"and {s.Hkv} key/value heads, fwd+bwd, numpy float64"}
 
     line = {
         "metric": "causal RoPE attention fwd+bwd TFLOP/s",
