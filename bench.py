@@ -40,7 +40,7 @@ def _parse():
     ap.add_argument("--steps", type=int, default=8)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: 7B shape)")
-    ap.add_argument("--cpu-rows", type=int, default=6144,
+    ap.add_argument("--cpu-rows", type=int, default=16384,
                     help="tokens of the workload the CPU oracle runs for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true", help="also print the per-kernel table")
@@ -274,18 +274,19 @@ def main():
         run.step(stream)
     torch.cuda.synchronize()
 
-    # Timed region: K steps between two events on the stream the library uses.
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    # Timed region: K steps between events on the stream the library uses
+    # (one event before the first step and one after each step).
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         run.step(stream)
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    ms_median = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]))
 
     # Per-kernel pass: the library brackets each launch with HIP events on
     # its stream; same K steps again.
@@ -352,6 +353,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(ms_median, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
