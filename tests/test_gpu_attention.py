@@ -49,6 +49,11 @@ SMALL = [
     synth.AttnShape("short sequences", T=111, seq_len=37, H=2, Hkv=2, seed=5),
     synth.AttnShape("long ragged", T=1100, seq_len=1100, H=2, Hkv=1, seed=6),
     synth.AttnShape("rope base 500000", T=256, seq_len=256, H=2, Hkv=2, base=500000.0, seed=7),
+    # tile edges: 64-row K/V and query tiles, 128-row query and key blocks
+    synth.AttnShape("seq 64", T=192, seq_len=64, H=2, Hkv=1, seed=8),
+    synth.AttnShape("seq 127", T=254, seq_len=127, H=2, Hkv=2, seed=9),
+    synth.AttnShape("seq 128", T=256, seq_len=128, H=1, Hkv=1, seed=10),
+    synth.AttnShape("seq 129", T=258, seq_len=129, H=8, Hkv=1, seed=11),
 ]
 
 
