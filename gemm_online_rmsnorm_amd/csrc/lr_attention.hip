@@ -190,10 +190,10 @@ __device__ __forceinline__ void col_offsets(int g, int s, uint32_t (&o)[8]) {
     o[i] = (uint32_t)(r0 * ROWB + 16 * ((2 * i + ((s >> 1) & 1)) ^ swz(r0)) + 8 * (s & 1));
 }
 
-// 16-byte row fragment at LDS byte `addr` + IMM.
-template <int IMM>
-__device__ __forceinline__ u32x4 frag_rows(const unsigned char* lds, uint32_t off) {
-  return *reinterpret_cast<const u32x4*>(lds + IMM + off);
+// 16-byte row fragment: `tile` points at the tile (plus 4096 kf for row
+// block kf), `off` is the lane's row offset (rowoff[st]).
+__device__ __forceinline__ u32x4 frag_rows(const unsigned char* tile, uint32_t off) {
+  return *reinterpret_cast<const u32x4*>(tile + off);
 }
 
 // Transposed fragment: lane (g, s) receives column 16 i + s of tile rows
@@ -217,14 +217,13 @@ __device__ __forceinline__ u32x4 frag_cols(uint32_t addr) {
 // delivers: the transposing reads are inline assembly, so without the tie
 // the compiler could schedule a product that uses a fragment before the
 // wait.
-__device__ __forceinline__ void lds_wait(u32x4 (&x)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])::"memory");
-}
 __device__ __forceinline__ void lds_wait(u32x4 (&x)[2]) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1])::"memory");
 }
 // The same, leaving the N most recent LDS reads in flight (LDS reads
-// return in order, so the older group's fragments have arrived).
+// return in order, so the older group's fragments have arrived). Scalar
+// loads share this counter and may return out of order; in these loops the
+// compiler has waited for its scalar loads before the fragment reads start.
 template <int N>
 __device__ __forceinline__ void lds_wait_keep(u32x4 (&x)[4]) {
   asm volatile("s_waitcnt lgkmcnt(%4)"
@@ -410,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     for (int stp = 0; stp < 4; ++stp)
 #pragma unroll
       for (int kf = 0; kf < 4; ++kf) {
-        const u32x4 kr = frag_rows<0>(lds + KO + 4096 * kf, roff[stp]);
+        const u32x4 kr = frag_rows(lds + KO + 4096 * kf, roff[stp]);
 #pragma unroll
         for (int f = 0; f < 2; ++f) s[f][kf] = mma(kr, qf[f][stp], s[f][kf]);
       }
@@ -642,8 +641,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
     for (int stp = 0; stp < 4; ++stp)
 #pragma unroll
       for (int kf = 0; kf < 4; ++kf) {
-        const u32x4 kr = frag_rows<0>(lds + KO + 4096 * kf, roff[stp]);
-        const u32x4 vr = frag_rows<0>(lds + VO + 4096 * kf, roff[stp]);
+        const u32x4 kr = frag_rows(lds + KO + 4096 * kf, roff[stp]);
+        const u32x4 vr = frag_rows(lds + VO + 4096 * kf, roff[stp]);
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
           sc[f][kf] = mma(kr, qf[f][stp], sc[f][kf]);
@@ -830,8 +829,8 @@ __global__ __launch_bounds__(64 * NWK, 1) void attn_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
           const int qf = 2 * t + qq;
-          const u32x4 qr = frag_rows<0>(lds + QO + 4096 * qf, roff[stp]);
-          const u32x4 dr = frag_rows<0>(lds + DO + 4096 * qf, roff[stp]);
+          const u32x4 qr = frag_rows(lds + QO + 4096 * qf, roff[stp]);
+          const u32x4 dr = frag_rows(lds + DO + 4096 * qf, roff[stp]);
 #pragma unroll
           for (int f = 0; f < FK; ++f) {
             sc[f][qq] = mma(qr, kf[f][stp], sc[f][qq]);
