@@ -54,6 +54,8 @@ SMALL = [
     synth.AttnShape("seq 127", T=254, seq_len=127, H=2, Hkv=2, seed=9),
     synth.AttnShape("seq 128", T=256, seq_len=128, H=1, Hkv=1, seed=10),
     synth.AttnShape("seq 129", T=258, seq_len=129, H=8, Hkv=1, seed=11),
+    # long sequence: positions up to 8191 (large rotation angles), 128 key tiles
+    synth.AttnShape("seq 8192", T=8192, seq_len=8192, H=2, Hkv=1, seed=12),
 ]
 
 
