@@ -47,9 +47,11 @@ def _parse():
     ap.add_argument("--tp-split", type=int, default=0, metavar="k",
                     help="instead of the block step: time one rank's GEMMs of the config's "
                          "block under the vanilla and the bottleneck-aware split over k ranks")
-    ap.add_argument("--attention", choices=("mha", "gqa"), default=None,
+    ap.add_argument("--attention", choices=("mha", "gqa", "block"), default=None,
                     help="instead of the block step: causal RoPE attention fwd+bwd at the "
-                         "LLaMA-2-7B attention shape (mha: 32 kv heads, gqa: 8)")
+                         "LLaMA-2-7B attention shape (mha: 32 kv heads, gqa: 8), or "
+                         "(block) the whole decoder block: the config's linear stack with "
+                         "attention between its stages")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"first make one device copy of {COPY_BYTES} bytes, the reference "
                          "rocprofv3 byte counters are scaled by")
@@ -118,6 +120,73 @@ def _blas_threads():
                     if i.get("user_api") == "blas"] or [1])
     except Exception:
         return len(os.sched_getaffinity(0))
+
+
+def block_attention_main(args):
+    """One JSON line: the whole decoder block, forward + backward: the
+    low-rank linear stack of the config (7B by default) split at the
+    attention core, with causal RoPE attention (4 sequences of 4096 tokens,
+    heads of 128) between the stages, as a trainer chains the entry points."""
+    import torch
+
+    import synth
+    import gemm_online_rmsnorm_amd as lr
+    from gemm_online_rmsnorm_amd.runner import BlockRun
+
+    s = synth.config(args.config)
+    if s.dtype != "bf16" or s.partials or s.d % 128 or s.T % 4096:
+        print("--attention block needs a bf16 full-block config with d a multiple of 128",
+              file=sys.stderr)
+        sys.exit(2)
+    heads, seq_len = s.d // 128, 4096
+    print(f"[bench] decoder block {s.name} with attention ({heads} heads of 128)",
+          file=sys.stderr, flush=True)
+    run = BlockRun(s.T, s.d, s.r, s.F, s.D, s.P, s.dtype, s.eps, s.partials, synth.make_inputs(s),
+                   heads=heads)
+    ashape = lr.attn_shape(s.T, seq_len, heads, heads, 128)
+    lse = torch.empty(heads, s.T, dtype=torch.float32, device="cuda")
+    wsf = torch.empty(lr.attention_workspace_bytes(ashape, False), dtype=torch.uint8,
+                      device="cuda")
+    wsb = torch.empty(lr.attention_workspace_bytes(ashape, True), dtype=torch.uint8,
+                      device="cuda")
+    stream = torch.cuda.current_stream()
+    Q, K, V = run.out["Q"], run.out["K"], run.out["V"]
+
+    def step():
+        run.fwd(stage=lr.LR_STAGE_PRE_ATTN, stream=stream)
+        lr.attention_fwd(ashape, Q, K, V, run.O, lse, ws=wsf, stream=stream)
+        run.fwd(stage=lr.LR_STAGE_POST_ATTN, stream=stream)
+        run.bwd(stage=lr.LR_STAGE_POST_ATTN, stream=stream)
+        lr.attention_bwd(ashape, Q, K, V, run.O, run.dO, lse, run.dQ, run.dK, run.dV, ws=wsb,
+                         stream=stream)
+        run.bwd(stage=lr.LR_STAGE_PRE_ATTN, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    pairs = (s.T // seq_len) * seq_len * (seq_len + 1) / 2
+    flop = s.T * (s.fwd_flop_per_token() + s.bwd_flop_per_token()
+                  + s.recompute_flop_per_token()) + 14 * 128 * pairs * heads
+    tflops = flop / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "whole decoder block (low-rank linear stack + causal RoPE attention) "
+                  "fwd+bwd tokens/s",
+        "value": round(s.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian inputs and random-init factors)",
+        "config": {"workload": f"{s.name} block with attention", "tokens": s.T,
+                   "seq_len": seq_len, "heads": heads, "d": s.d, "r": s.r, "d_ff": s.F},
+        "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+    }), flush=True)
 
 
 def attention_main(args):
@@ -250,6 +319,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     lr._lib.load()
+    if args.attention == "block":
+        block_attention_main(args)
+        return
     if args.attention:
         attention_main(args)
         return
