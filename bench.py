@@ -52,6 +52,9 @@ def _parse():
                          "LLaMA-2-7B attention shape (mha: 32 kv heads, gqa: 8), or "
                          "(block) the whole decoder block: the config's linear stack with "
                          "attention between its stages")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step into a HIP graph and time K replays of it "
+                         "instead of K eager steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"first make one device copy of {COPY_BYTES} bytes, the reference "
                          "rocprofv3 byte counters are scaled by")
@@ -113,6 +116,31 @@ def tp_split_main(args, s):
     print(json.dumps(out))
 
 
+def _graph(torch, step):
+    """Capture step(None) (every library call on the current stream) into a
+    HIP graph, after one eager call on the capture's side stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(None)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(None)
+    torch.cuda.synchronize()
+    return g
+
+
+def _timed_step(torch, args, step, stream):
+    """What one timed step runs: an eager step on `stream`, or with --graph a
+    replay (on the current stream, which is `stream`) of its captured graph."""
+    if not args.graph:
+        return lambda: step(stream)
+    g = _graph(torch, step)
+    return g.replay
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -152,23 +180,24 @@ def block_attention_main(args):
     stream = torch.cuda.current_stream()
     Q, K, V = run.out["Q"], run.out["K"], run.out["V"]
 
-    def step():
-        run.fwd(stage=lr.LR_STAGE_PRE_ATTN, stream=stream)
-        lr.attention_fwd(ashape, Q, K, V, run.O, lse, ws=wsf, stream=stream)
-        run.fwd(stage=lr.LR_STAGE_POST_ATTN, stream=stream)
-        run.bwd(stage=lr.LR_STAGE_POST_ATTN, stream=stream)
+    def step(st):
+        run.fwd(stage=lr.LR_STAGE_PRE_ATTN, stream=st)
+        lr.attention_fwd(ashape, Q, K, V, run.O, lse, ws=wsf, stream=st)
+        run.fwd(stage=lr.LR_STAGE_POST_ATTN, stream=st)
+        run.bwd(stage=lr.LR_STAGE_POST_ATTN, stream=st)
         lr.attention_bwd(ashape, Q, K, V, run.O, run.dO, lse, run.dQ, run.dK, run.dV, ws=wsb,
-                         stream=stream)
-        run.bwd(stage=lr.LR_STAGE_PRE_ATTN, stream=stream)
+                         stream=st)
+        run.bwd(stage=lr.LR_STAGE_PRE_ATTN, stream=st)
 
     for _ in range(args.warmup):
-        step()
+        step(stream)
+    timed = _timed_step(torch, args, step, stream)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
-        step()
+        timed()
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
@@ -181,6 +210,7 @@ def block_attention_main(args):
                   "fwd+bwd tokens/s",
         "value": round(s.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "launch": "hip graph" if args.graph else "eager",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded Gaussian inputs and random-init factors)",
         "config": {"workload": f"{s.name} block with attention", "tokens": s.T,
@@ -216,25 +246,26 @@ def attention_main(args):
                       device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step():
-        lr.attention_fwd(shape, Q, K, V, O, lse, ws=wsf, stream=stream)
-        lr.attention_bwd(shape, Q, K, V, O, dO, lse, dQ, dK, dV, ws=wsb, stream=stream)
+    def step(st):
+        lr.attention_fwd(shape, Q, K, V, O, lse, ws=wsf, stream=st)
+        lr.attention_bwd(shape, Q, K, V, O, dO, lse, dQ, dK, dV, ws=wsb, stream=st)
 
     for _ in range(args.warmup):
-        step()
+        step(stream)
+    timed = _timed_step(torch, args, step, stream)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
-        step()
+        timed()
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
 
     lr.profile_enable(True)
     for _ in range(args.steps):
-        step()
+        step(stream)
     torch.cuda.synchronize()
     lr.profile_enable(False)
     prof = lr.profile_collect()
@@ -280,6 +311,7 @@ def attention_main(args):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "launch": "hip graph" if args.graph else "eager",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -344,6 +376,7 @@ def main():
 
     for _ in range(args.warmup):
         run.step(stream)
+    timed = _timed_step(torch, args, run.step, stream)
     torch.cuda.synchronize()
 
     # Timed region: K steps between events on the stream the library uses
@@ -353,7 +386,7 @@ def main():
     w0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(args.steps):
-        run.step(stream)
+        timed()
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -426,6 +459,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "ms_per_step_median": round(ms_median, 4),
+        "launch": "hip graph" if args.graph else "eager",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

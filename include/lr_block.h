@@ -26,6 +26,11 @@
  *     re-entrant across streams. Caller-provided workspace must not be used
  *     by two calls that may run concurrently.
  *   - Outputs are overwritten, never accumulated into.
+ *   - A call enqueues kernel launches only (no memset, copy, allocation or
+ *     synchronisation), so a sequence of calls may be captured into a HIP
+ *     graph (hipStreamBeginCapture) and replayed. The first call of an entry
+ *     point on a device may set kernel attributes; make it outside capture.
+ *     The kernels are deterministic: the same inputs give the same bits.
  *   - Arguments are validated before anything is enqueued; on failure the
  *     call returns a negative status, enqueues nothing and records a
  *     message for lr_last_error(). A failed kernel launch returns
