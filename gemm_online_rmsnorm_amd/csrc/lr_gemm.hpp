@@ -219,8 +219,9 @@ __device__ __forceinline__ void mfma_step<float>(const u32x4& a, const u32x4& b,
 // hardware deals workgroups to the 8 XCDs round-robin) get consecutive
 // logical ids, which walk GROUP_M M-tiles before the next N-tile so that the
 // XCD's L2 serves both operands' tiles to several workgroups.
+template <int GROUP_M = 8>
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int NXCD = 8, GROUP_M = 8;
+  constexpr int NXCD = 8;
   const int nwg = tiles_m * tiles_n;
   const int pid = blockIdx.x;
   const int q = nwg / NXCD, rem = nwg % NXCD;

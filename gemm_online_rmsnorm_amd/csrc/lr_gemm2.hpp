@@ -514,7 +514,11 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   const int wave = wave_uniform(tid >> 6);
   const int wm = wave / TL::NWN, wn = wave % TL::NWN;
   int tm, tn;
-  tile_coords(g.tiles_m, g.tiles_n, tm, tn);
+  // An XCD's 32 concurrent tiles span 4 M-tiles x 8 N-tiles. For the split
+  // tile, whose rows carry two A operands, that is 7.3 MB of operands at the
+  // 7B shape against 8.4 MB for 8 x 4 (measured: 6% faster SwiGLU tiles,
+  // 2-6% faster one-pair tiles, 5% fewer L2 misses).
+  tile_coords<4>(g.tiles_m, g.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BNO;
   const int slot = (NPAIR == 1) ? (int)blockIdx.z % g.groups : 0;
   const int split = (int)blockIdx.z / g.groups;
