@@ -141,6 +141,29 @@ def _timed_step(torch, args, step, stream):
     return g.replay
 
 
+def _calibration_copy(torch):
+    """One device copy of COPY_BYTES: the reference rocprofv3's byte counters
+    are scaled by (gemm_online_rmsnorm_amd/traffic.py)."""
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _traffic_record(bench_name):
+    """Measured HBM bytes per launch of the named launch, from the record in
+    profiles/ taken on the current kernel sources; None without one."""
+    from gemm_online_rmsnorm_amd import traffic as lrtraffic
+    if not os.path.isdir(TRAFFIC_DIR):
+        return None
+    for name in sorted(os.listdir(TRAFFIC_DIR)):
+        if name.startswith("traffic_") and name.endswith(".json"):
+            rec = lrtraffic.load(os.path.join(TRAFFIC_DIR, name))
+            if rec and rec.get("bench_name") == bench_name:
+                return rec["traffic_bytes"]
+    return None
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -245,6 +268,8 @@ def attention_main(args):
     wsb = torch.empty(lr.attention_workspace_bytes(shape, True), dtype=torch.uint8,
                       device="cuda")
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        _calibration_copy(torch)
 
     def step(st):
         lr.attention_fwd(shape, Q, K, V, O, lse, ws=wsf, stream=st)
@@ -285,6 +310,14 @@ def attention_main(args):
             rec["gbs"] = round(2 * s.T * heads * s.dh * 2 / (per * 1e-3) / 1e9, 1)
         kernels.append(rec)
     dom = max((k for k in kernels if "tflops" in k), key=lambda k: k["step_ms"])
+    # Algorithmic HBM bytes per launch: each tensor read or written once.
+    qb, kb, rowb = s.T * s.H * s.dh * 2, s.T * s.Hkv * s.dh * 2, s.T * s.H * 4
+    attn_bytes = {"attention fwd": qb + 2 * kb + qb + rowb,
+                  "attention bwd dQ": 3 * qb + 2 * kb + rowb + qb + 2 * rowb,
+                  "attention bwd dK dV": 2 * qb + 2 * kb + 2 * rowb + 2 * kb}
+    traffic, traffic_alg = _traffic_record(dom["kernel"]), None
+    if traffic is not None:
+        traffic_alg = attn_bytes[dom["kernel"]]
     flop = 14 * s.dh * pairs * s.H
     tflops = flop / (ms * 1e-3) / 1e12
 
@@ -322,8 +355,8 @@ def attention_main(args):
         "mfma_peak_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": {"kernel": dom["kernel"], "bound": "mfma", "achieved": dom["tflops"],
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(dom["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "ms_per_launch": dom["ms"]},
+                     "frac": round(dom["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "traffic_algorithmic_bytes": traffic_alg, "ms_per_launch": dom["ms"]},
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
@@ -368,11 +401,7 @@ def main():
                    heads=s.heads)
     stream = torch.cuda.current_stream()
     if args.copy_calibration:
-        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        _calibration_copy(torch)
 
     for _ in range(args.warmup):
         run.step(stream)
@@ -429,13 +458,9 @@ def main():
     }
     # Measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE,
     # copy-calibrated), when taken on the current kernel sources.
-    from gemm_online_rmsnorm_amd import traffic as lrtraffic
-    for name in sorted(os.listdir(TRAFFIC_DIR)) if os.path.isdir(TRAFFIC_DIR) else []:
-        if name.startswith("traffic_") and name.endswith(".json"):
-            rec = lrtraffic.load(os.path.join(TRAFFIC_DIR, name))
-            if rec and rec.get("bench_name") == dom["kernel"]:
-                roofline["traffic"] = rec["traffic_bytes"]
-                roofline["traffic_algorithmic_bytes"] = round(work[dom["kernel"]][1])
+    roofline["traffic"] = _traffic_record(dom["kernel"])
+    if roofline["traffic"] is not None:
+        roofline["traffic_algorithmic_bytes"] = round(work[dom["kernel"]][1])
     roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
 
     flop_step = s.T * (s.fwd_flop_per_token() + s.bwd_flop_per_token()

@@ -34,13 +34,15 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 # code (the attention kernels and the C ABI layer are built from other files).
 KERNEL_SOURCES = ("lr_kernels.hip", "lr_common.hpp", "lr_gemm.hpp", "lr_gemm2.hpp",
                   "lr_internal.hpp")
+# Sources of the attention kernels and their launch code.
+ATTENTION_SOURCES = ("lr_attention.hip", "lr_attn.hpp")
 
 
-def source_hash() -> str:
-    """SHA-256 over the sources the block's kernels are built from."""
+def source_hash(sources=KERNEL_SOURCES) -> str:
+    """SHA-256 over the named kernel sources (files of csrc/)."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name in KERNEL_SOURCES:
+        if name in sources:
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -65,7 +67,8 @@ def _match(table: dict, needle: str) -> list[tuple[int, float]]:
     return table[hits[0]]
 
 
-def measure(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int) -> dict:
+def measure(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int,
+            sources=KERNEL_SOURCES) -> dict:
     fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
     write = _per_dispatch(write_csv, "WRITE_SIZE")
     kf, kw = _match(fetch, kernel), _match(write, kernel)
@@ -86,7 +89,7 @@ def measure(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int) -> dic
         "traffic_bytes": round(fetch_b + write_b),
         "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
         "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
-        "source_sha256": source_hash(),
+        "sources": list(sources), "source_sha256": source_hash(sources),
     }
 
 
@@ -97,7 +100,8 @@ def load(path: str) -> dict | None:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    return rec if rec.get("source_sha256") == source_hash() else None
+    sources = tuple(rec.get("sources", KERNEL_SOURCES))
+    return rec if rec.get("source_sha256") == source_hash(sources) else None
 
 
 def main() -> None:
@@ -108,9 +112,12 @@ def main() -> None:
     ap.add_argument("--bench-name", required=True, help="the launch's name in bench.py")
     ap.add_argument("--copy-bytes", type=int, required=True)
     ap.add_argument("--command", default="", help="the profiled command, for the record")
+    ap.add_argument("--attention", action="store_true",
+                    help="an attention kernel: hash the attention sources")
     ap.add_argument("-o", "--out", required=True)
     a = ap.parse_args()
-    rec = measure(a.fetch_csv, a.write_csv, a.kernel, a.copy_bytes)
+    rec = measure(a.fetch_csv, a.write_csv, a.kernel, a.copy_bytes,
+                  ATTENTION_SOURCES if a.attention else KERNEL_SOURCES)
     rec["bench_name"] = a.bench_name
     rec["command"] = a.command
     with open(a.out, "w") as f:

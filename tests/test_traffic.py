@@ -57,3 +57,22 @@ def test_stale_record_is_ignored(tmp_path):
     assert traffic.load(str(p)) is None
     p.write_text(json.dumps({"source_sha256": traffic.source_hash(), "traffic_bytes": 1}))
     assert traffic.load(str(p))["traffic_bytes"] == 1
+
+
+def test_record_follows_its_own_sources(tmp_path):
+    """A record names the sources it was taken on; it is valid while they are
+    unchanged, whichever kernel family it covers."""
+    import json
+    k = "attn_dkdv_kernel"
+    _csv(tmp_path / "f.csv", "FETCH_SIZE", [(traffic.COPY_KERNEL, 64, 512.0), (k, 512, 10.0)])
+    _csv(tmp_path / "w.csv", "WRITE_SIZE", [(traffic.COPY_KERNEL, 64, 1024.0), (k, 512, 5.0)])
+    rec = traffic.measure(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), k, 1 << 20,
+                          traffic.ATTENTION_SOURCES)
+    assert rec["sources"] == list(traffic.ATTENTION_SOURCES)
+    assert rec["source_sha256"] == traffic.source_hash(traffic.ATTENTION_SOURCES)
+    assert rec["source_sha256"] != traffic.source_hash()
+    path = tmp_path / "rec.json"
+    path.write_text(json.dumps(rec))
+    assert traffic.load(str(path)) == rec
+    path.write_text(json.dumps(rec | {"source_sha256": "0" * 64}))
+    assert traffic.load(str(path)) is None
