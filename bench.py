@@ -55,6 +55,10 @@ def _parse():
     ap.add_argument("--graph", action="store_true",
                     help="capture one step into a HIP graph and time K replays of it "
                          "instead of K eager steps")
+    ap.add_argument("--vendor-gemms", action="store_true",
+                    help="instead of the block step: time torch.matmul (hipBLASLt) on plain "
+                         "GEMMs of the config's shapes, a reference point for the library's "
+                         "fused kernels (no fusion, random operands)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"first make one device copy of {COPY_BYTES} bytes, the reference "
                          "rocprofv3 byte counters are scaled by")
@@ -162,6 +166,51 @@ def _traffic_record(bench_name):
             if rec and rec.get("bench_name") == bench_name:
                 return rec["traffic_bytes"]
     return None
+
+
+def vendor_gemms_main(args, s):
+    """One JSON line: torch.matmul (hipBLASLt on ROCm) on plain bf16 GEMMs
+    with the shapes of the block's products, each timed over K calls after
+    W warm-up calls. Nothing here is part of the library's path."""
+    import torch
+
+    T, d, r, F = s.T, s.d, s.r, s.F
+    shapes = [  # name, M, N, K, operand layout
+        ("QKV down-projection (3r x d)", T, 3 * r, d, "NT"),
+        ("one up-projection (d x r)", T, d, r, "NT"),
+        ("one gate/up up-projection (d_ff x r)", T, F, r, "NT"),
+        ("down-projection (r x d_ff)", T, r, F, "NT"),
+        ("weight gradient dB_g (d_ff x r over T)", F, r, T, "TN"),
+        ("weight gradient dB_dn (d x r over T)", d, r, T, "TN"),
+    ]
+    g = torch.Generator(device="cuda").manual_seed(0)
+    out = []
+    for name, M, N, K, lay in shapes:
+        if lay == "NT":
+            a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+            b = torch.randn(N, K, device="cuda", dtype=torch.bfloat16, generator=g)
+            fn = lambda a=a, b=b: a @ b.t()
+        else:
+            a = torch.randn(K, M, device="cuda", dtype=torch.bfloat16, generator=g)
+            b = torch.randn(K, N, device="cuda", dtype=torch.bfloat16, generator=g)
+            fn = lambda a=a, b=b: a.t() @ b
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        out.append({"gemm": name, "M": M, "N": N, "K": K, "layout": lay, "ms": round(ms, 4),
+                    "tflops": round(2 * M * N * K / (ms * 1e-3) / 1e12, 1)})
+        del a, b
+    print(json.dumps({"metric": "torch.matmul (hipBLASLt) bf16 TFLOP/s on the block's GEMM "
+                                "shapes (reference point)", "n_gpus": 1,
+                      "config": {"workload": s.name, "tokens": T, "d": d, "r": r, "d_ff": F},
+                      "gemms": out}), flush=True)
 
 
 def _blas_threads():
@@ -391,6 +440,9 @@ def main():
         attention_main(args)
         return
     s = synth.config(args.config)
+    if args.vendor_gemms:
+        vendor_gemms_main(args, s)
+        return
     if args.tp_split:
         tp_split_main(args, s)
         return
