@@ -48,10 +48,16 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 // pair 1's; waves of the first NWN / 2 columns multiply pair 0, the others
 // pair 1. Each wave runs one pair, so the LDS reads per MFMA are those of a
 // one-pair tile twice the size; the epilogue pairs up the two halves.
-template <int BM_, int BN_, int BK_, int NWM_, int NWN_, int NSTAGE_, int NSPLIT_ = 1>
+template <int BM_, int BN_, int BK_, int NWM_, int NWN_, int NSTAGE_, int NSPLIT_ = 1,
+          int NSTAGE_A_ = 0>
 struct Tile2 {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, NWM = NWM_, NWN = NWN_;
   static constexpr int NSTAGE = NSTAGE_;
+  // NSTAGE_A_ > 0: the A operand (the streamed activation of a one-pair
+  // product) gets a ring of its own with NSTAGE_A_ stages and B keeps
+  // NSTAGE, so A's loads are issued NSTAGE_A_ - 1 K-tiles ahead.
+  static constexpr bool ASYM = NSTAGE_A_ > 0;
+  static constexpr int NSTAGE_A = ASYM ? NSTAGE_A_ : NSTAGE_;
   static constexpr int NSPLIT = NSPLIT_;
   static constexpr int BNO = BN / NSPLIT;  // output columns of a block tile
   static_assert(NSPLIT == 1 || (NSPLIT == 2 && NWN % 2 == 0), "split tiles need an even NWN");
@@ -423,6 +429,13 @@ template <class TL, int NPAIR>
 constexpr int stage_bytes() {
   return (TL::NSPLIT == 2 ? 2 * TL::BM + TL::BN : NPAIR * (TL::BM + TL::BN)) * TL::BK * 2;
 }
+// The operand ring: NSTAGE stages, or with separate rings NSTAGE_A A tiles
+// followed by NSTAGE B tiles.
+template <class TL, int NPAIR>
+constexpr int ring_bytes() {
+  return TL::ASYM ? (TL::NSTAGE_A * TL::BM + TL::NSTAGE * TL::BN) * TL::BK * 2
+                  : TL::NSTAGE * stage_bytes<TL, NPAIR>();
+}
 
 // Wave-private epilogue staging: one 16-row band of a wave tile in bf16.
 template <class TL>
@@ -470,7 +483,7 @@ constexpr int epi_pds() {
 }
 template <class TL, int NPAIR, int EPI>
 constexpr int gemm2_body_bytes() {
-  constexpr int ring = TL::NSTAGE * stage_bytes<TL, NPAIR>();
+  constexpr int ring = ring_bytes<TL, NPAIR>();
   constexpr int in_end = epi_in0<TL, EPI>() + TL::NWAVE * epi_pds<TL, EPI>() * epi_nin<EPI>() * 2048;
   constexpr int epi = in_end > epi_area_bytes<TL>() ? in_end : epi_area_bytes<TL>();
   return ring > epi ? ring : epi;
@@ -499,7 +512,9 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   constexpr int BNO = TL::BNO;
   constexpr int SB = stage_bytes<TL, NPAIR>();
   extern __shared__ __align__(16) unsigned char lds[];
-  constexpr int RING = S * SB;
+  constexpr int RING = ring_bytes<TL, NPAIR>();
+  static_assert(!TL::ASYM || (NPAIR == 1 && !SPLITN), "separate rings are for one-pair tiles");
+  constexpr int SA = TL::NSTAGE_A;
   // Epilogue areas (the ring is free by then): staging bands and column
   // sums, the split-tile exchange, the band-input slots.
   constexpr int EPIB = epi_area_bytes<TL>();
@@ -596,6 +611,26 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     }
   }
   auto stage_ptr = [&](int s) { return lds + s * SB; };
+  // Stage tiles of K-tile kt: [A][B] stages, or the two rings.
+  auto a_stage = [&](int kt) {
+    return TL::ASYM ? lds + (kt % SA) * (BM * BK * 2) : stage_ptr(kt % S);
+  };
+  auto b_stage = [&](int kt) {
+    return TL::ASYM ? lds + SA * (BM * BK * 2) + (kt % S) * (BNO * BK * 2)
+                    : stage_ptr(kt % S) + BM * BK * 2;
+  };
+  // Separate rings: one operand's loads of K-tile kt (the same empty range
+  // past the last K-tile as below).
+  auto issue_a = [&](int kt) {
+    if (NDMA < TL::NWAVE && wave >= NDMA) return;
+    const uint32_t n = kt < g.ktiles_split ? (uint32_t)(2 * (ea[0] - kt * sa[0])) : 0u;
+    a0.issue(pa[0] + kt * sa[0], n, a_stage(kt), wave);
+  };
+  auto issue_b = [&](int kt) {
+    if (NDMA < TL::NWAVE && wave >= NDMA) return;
+    const uint32_t n = kt < g.ktiles_split ? (uint32_t)(2 * (eb[0] - kt * sb[0])) : 0u;
+    b0.issue(pb[0] + kt * sb[0], n, b_stage(kt), wave);
+  };
   auto issue = [&](int kt) {
     if (NDMA < TL::NWAVE && wave >= NDMA) return;
     unsigned char* st = stage_ptr(kt % S);
@@ -659,10 +694,13 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   // first fragments of the next K-tile load under that sub-step's MFMAs.
   constexpr int Q = (SPLITN ? 1 : NPAIR) * TL::NSTEP;
   u32x4 fa[2][FM], fb[2][FN];
-  auto read_q = [&](const unsigned char* st, int q, int buf) {
+  // st: the stage of K-tile kt (one ring); separate rings use kt.
+  auto read_q = [&](int kt, const unsigned char* st, int q, int buf) {
     const int p = q / TL::NSTEP, s = q % TL::NSTEP;
-    const unsigned char* tA = SPLITN ? st + pw * BM * BK * 2 : st + p * (BM + BN) * BK * 2;
-    const unsigned char* tB = SPLITN ? st + 2 * BM * BK * 2 : tA + BM * BK * 2;
+    const unsigned char* tA = TL::ASYM ? a_stage(kt)
+                              : SPLITN ? st + pw * BM * BK * 2 : st + p * (BM + BN) * BK * 2;
+    const unsigned char* tB = TL::ASYM ? b_stage(kt)
+                              : SPLITN ? st + 2 * BM * BK * 2 : tA + BM * BK * 2;
     const bool amc = (MCMASK >> (2 * p)) & 1u;
     const bool bmc = (MCMASK >> (2 * p + 1)) & 1u;
 #pragma unroll
@@ -725,12 +763,28 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   constexpr int NDS = ((MCMASK & 1u) ? 0 : FM) + ((MCMASK & 2u) ? 0 : FN);
 
   const int nk = g.ktiles_split;
+  // Separate rings (A: SA = 3 stages, B: S = 2): at the barrier of K-tile kt
+  // B of K-tile kt + 2 is issued, then A of kt + 3, so the loads issued
+  // after K-tile kt + 1's are A's of kt + 2 alone.
+  static_assert(!TL::ASYM || (SA == 3 && S == 2), "separate rings: 3 A stages, 2 B stages");
+  constexpr int LA = OA0::PER;
+  static_assert(!TL::ASYM || 2 * LA + OB0::PER < 64, "too many loads in flight for vmcnt");
+  if constexpr (TL::ASYM) {
+    issue_a(0);
+    issue_b(0);
+    issue_a(1);
+    wait_vmcnt<LA>();
+    block_barrier();
+    issue_b(1);
+    issue_a(2);
+  } else {
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s) issue(s);
-  wait_vmcnt<VM_AFTER>();
-  block_barrier();
-  issue(S - 1);
-  read_q(stage_ptr(0), 0, 0);
+    for (int s = 0; s < S - 1; ++s) issue(s);
+    wait_vmcnt<VM_AFTER>();
+    block_barrier();
+    issue(S - 1);
+  }
+  read_q(0, stage_ptr(0), 0, 0);
   // Fragment reads are in flight only inside the loop body, between a
   // sub-step's start and the next sub-step's wait: every path into and out
   // of the loop has them landed, so code the compiler places at the loop's
@@ -755,7 +809,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       wait_lgkmcnt0();
       sched_fence();
       if (q + 1 < Q) {
-        read_q(st, q + 1, buf ^ 1);
+        read_q(kt, st, q + 1, buf ^ 1);
         compute_q(q, buf);
         interleave<NDS, 0, FM * FN>();
       } else {
@@ -763,10 +817,17 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
         // passes the barrier; the stage of K-tile kt is then free for
         // K-tile kt + S, and K-tile kt + 1 has landed. (On the last K-tile
         // this reads a stage no MFMA uses.)
-        wait_vmcnt<VM_AFTER>();
-        block_barrier();
-        issue(kt + S);
-        read_q(stage_ptr((kt + 1) % S), 0, buf ^ 1);
+        if constexpr (TL::ASYM) {
+          wait_vmcnt<LA>();
+          block_barrier();
+          issue_b(kt + 2);
+          issue_a(kt + 3);
+        } else {
+          wait_vmcnt<VM_AFTER>();
+          block_barrier();
+          issue(kt + S);
+        }
+        read_q(kt + 1, stage_ptr((kt + 1) % S), 0, buf ^ 1);
         compute_q(q, buf);
         interleave<NDS, L, FM * FN>();
       }
