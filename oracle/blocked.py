@@ -29,6 +29,15 @@ def grouped_views(fwd):
             np.concatenate([fwd["g_r"], fwd["u_r"]], axis=1))
 
 
+def _accumulate(acc, grads):
+    """Add one row block's weight and gamma gradients into the running sums.
+
+    The gradients are sums over tokens (project page, "Three supporting
+    changes": the weights see every token), so the blocks' parts add up."""
+    for k, v in grads.items():
+        acc[k] = v if k not in acc else acc[k] + v
+
+
 def _weights64(inp):
     return {n: np.asarray(inp[n], dtype=np.float64) for n in _WEIGHTS}
 
@@ -95,8 +104,7 @@ def run_fwd_bwd(inp, *, D: int, eps: float, n_panels: int = 1,
                     dA_o=g["A_o"], dB_o=g["B_o"],
                     dA_gu=np.concatenate([g["A_g"], g["A_u"]], axis=0),
                     dB_g=g["B_g"], dB_u=g["B_u"], dA_dn=g["A_dn"], dB_dn=g["B_dn"])
-                for k, v in wg.items():
-                    acc[k] = v if k not in acc else acc[k] + v
+                _accumulate(acc, wg)
         if on_rows is not None:
             on_rows(sel, loc)
         else:
