@@ -8,8 +8,16 @@ in HBM. Prints ONE JSON line:
   tflops         algorithmic TFLOP/s including the mandated recompute
   roofline       the dominant kernel against the bf16 MFMA peak, from HIP
                  events recorded around its launches on its stream
+  hbm_phases     every memory-bound kernel (row dots, gamma folds, split-K
+                 sums, column sums, rank-share finalize): GPU-side time per
+                 launch (20 launches back to back between two events),
+                 algorithmic bytes, GB/s and fraction of HBM bandwidth
   cpu_baseline   the fp64 CPU oracle on a bounded sample of the same
-                 workload, on this host's cores
+                 workload (all 16384 tokens by default), on this host's cores
+  parity         the outputs of the timed configuration against that oracle
+                 run: max|gpu - oracle| / max|oracle| over every output,
+                 saved activation and gradient; the exit status is 3 when
+                 it exceeds 1e-2 (bf16) or 1e-5 (fp32)
 
     python bench.py [--steps 8] [--warmup 2] [--config 3]
 
@@ -31,6 +39,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 MFMA_FP32_PEAK_TFLOPS = 157.3    # MI355X dense fp32
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 COPY_BYTES = 1 << 30             # calibration copy for the byte counters
+HBM_REPEAT = 20                  # back-to-back launches per memory-bound measurement
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -65,16 +74,24 @@ def _parse():
     return ap.parse_args()
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(s, inputs, rows):
-    """The oracle as it stands, timed on a bounded sample of the workload."""
+    """The oracle as it stands, timed on a bounded sample of the workload.
+    Returns the cpu_baseline record and the oracle's outputs (for parity)."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = _blas_threads()
     rows = min(rows, s.T)
     sample = {k: (v[:rows] if v.shape[0] == s.T and k in ("X", "O", "dY", "dQ", "dK", "dV")
                   else v) for k, v in inputs.items()}
@@ -83,10 +100,35 @@ def cpu_baseline(s, inputs, rows):
                              row_block=2048)
     dt = time.perf_counter() - t0
     assert np.isfinite(out["dA_qkv"]).all()
-    return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 2),
-            "sample": f"first {rows} of {s.T} tokens of the {s.name} workload, full fwd+bwd "
-                      f"incl. weight grads, numpy float64 (OpenBLAS)"}
+    rec = {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "seconds": round(dt, 2), "cpu_model": _cpu_model(),
+           "host_cpus": len(os.sched_getaffinity(0)),
+           "sample": f"first {rows} of {s.T} tokens of the {s.name} workload, full fwd+bwd "
+                     f"incl. weight grads, numpy float64 (OpenBLAS, {threads} threads)"}
+    return rec, out, rows
+
+
+def parity(gpu, ref, rows, T, tol):
+    """max|gpu - oracle| / max|oracle| per tensor on the oracle's rows (every
+    tensor, weight gradients included, when it ran all T rows)."""
+    import numpy as np
+    worst_k, worst, errs = None, 0.0, {}
+    for k, v in ref.items():
+        g = gpu[k]
+        if rows < T:
+            if k.startswith("d") and k not in ("dX", "dO"):
+                continue  # weight and gamma gradients need every row
+            g = g[:, :rows] if k.startswith("ss_panels") else g[:rows]
+        den = float(np.max(np.abs(v))) or 1.0
+        e = float(np.max(np.abs(np.asarray(g, dtype=np.float64) - v))) / den
+        if not np.all(np.isfinite(g)):
+            e = float("inf")
+        errs[k] = e
+        if not e <= worst:
+            worst_k, worst = k, e
+    return {"worst": worst, "tensor": worst_k, "tol": tol, "n_tensors": len(errs),
+            "rows": rows, "ok": bool(worst <= tol),
+            "metric": "max|gpu - oracle| / max|oracle| per tensor, fp64 oracle"}
 
 
 def tp_split_main(args, s):
@@ -427,7 +469,7 @@ def main():
     import synth
     import gemm_online_rmsnorm_amd as lr
     from gemm_online_rmsnorm_amd.runner import BlockRun
-    from gemm_online_rmsnorm_amd.work import MEMORY_BOUND, kernel_work
+    from gemm_online_rmsnorm_amd.work import is_memory_bound, kernel_work
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -493,11 +535,30 @@ def main():
             "ms": round(per, 4),
             "tflops": round(fl / (per * 1e-3) / 1e12, 1) if fl else None,
             "gbs": round(by / (per * 1e-3) / 1e9, 1),
-            "bound": "hbm" if name in MEMORY_BOUND else "mfma",
+            "bound": "hbm" if is_memory_bound(name) else "mfma",
             "step_ms": round(total / args.steps, 4),
         })
     kernel_ms = sum(k["step_ms"] for k in kernels)
     dom = max(kernels, key=lambda k: k["step_ms"])
+
+    # Memory-bound kernels, GPU-side: a pass in which each of them is
+    # enqueued HBM_REPEAT times back to back between its events, so the
+    # per-launch time leaves out the launch latency of a single launch.
+    lr.profile_repeat(HBM_REPEAT)
+    lr.profile_enable(True)
+    for _ in range(min(args.steps, 3)):
+        run.step(stream)
+    torch.cuda.synchronize()
+    lr.profile_enable(False)
+    lr.profile_repeat(1)
+    hbm = []
+    for name, count, total, nbytes in lr.profile_collect(with_bytes=True):
+        if not is_memory_bound(name) or count == 0 or total <= 0:
+            continue
+        gbs = nbytes / (total * 1e-3) / 1e9
+        hbm.append({"kernel": name, "us": round(1e3 * total / count, 2),
+                    "bytes": round(nbytes / count), "gbs": round(gbs, 1),
+                    "frac": round(gbs / HBM_PEAK_GBS, 3)})
     peak = MFMA_BF16_PEAK_TFLOPS if s.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
     roofline = {
         "kernel": dom["kernel"],
@@ -519,13 +580,17 @@ def main():
                        + s.recompute_flop_per_token())
     flop_model = s.T * 3 * s.fwd_flop_per_token()
     tflops = flop_step / (ms * 1e-3) / 1e12
-    mem = [k for k in kernels if k["bound"] == "hbm" and k["kernel"].startswith("row dot")]
 
-    cpu = None
+    cpu, par = None, None
     if not args.no_cpu_baseline:
         print("[bench] cpu_baseline: timing the fp64 oracle on a sample", file=sys.stderr,
               flush=True)
-        cpu = cpu_baseline(s, inputs, args.cpu_rows)
+        gpu_out = run.results(host_dtype=np.float32)
+        cpu, ref, rows = cpu_baseline(s, inputs, args.cpu_rows)
+        # The outputs of the last step of the passes above; every step
+        # recomputes them from the same inputs.
+        par = parity(gpu_out, ref, rows, s.T, 1e-2 if s.dtype == "bf16" else 1e-5)
+        del gpu_out, ref
 
     line = {
         "metric": "fwd+bwd low-rank block tokens/s + TFLOP/s as % of MI355X bf16 MFMA peak",
@@ -549,16 +614,20 @@ def main():
         "tflops_model": round(flop_model / (ms * 1e-3) / 1e12, 1),
         "mfma_peak_frac": round(tflops / peak, 4),
         "roofline": roofline,
-        "rowdot_hbm": [{"kernel": k["kernel"], "gbs": k["gbs"],
-                        "frac": round(k["gbs"] / HBM_PEAK_GBS, 3)} for k in mem],
+        "hbm_phases": hbm,
         "kernel_ms_sum": round(kernel_ms, 4),
         "wall_s": round(wall, 3),
+        "parity": par,
         "cpu_baseline": cpu,
     }
     if args.kernels:
         for k in sorted(kernels, key=lambda k: -k["step_ms"]):
             print(json.dumps(k), file=sys.stderr)
     print(json.dumps(line), flush=True)
+    if par is not None and not par["ok"]:
+        print(f"[bench] parity FAILED: {par['tensor']} off by {par['worst']:.3e} "
+              f"(tol {par['tol']})", file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import (  # noqa: F401
     LR_BF16, LR_EPI_ADD_RESIDUAL, LR_EPI_NONE, LR_EPI_ROW_SCALE, LR_EPI_SWIGLU_PAIR, LR_F32,
     LR_LAYOUT_NN, LR_LAYOUT_NT, LR_LAYOUT_TN, LR_STAGE_ALL, LR_STAGE_POST_ATTN,
-    LR_STAGE_PRE_ATTN, LRError, lr_block_shape,
+    LR_STAGE_PRE_ATTN, LR_WS_H, LR_WS_M, LRError, lr_block_shape,
 )
 
 WEIGHT_FIELDS = ("gamma1", "gamma2", "A_qkv", "B_q", "B_k", "B_v", "A_o", "B_o",
@@ -58,6 +58,19 @@ def block_shape(T, d, r, d_ff, d_norm=None, n_panels=1, n_heads=1, eps=1e-5, dty
 
 def workspace_bytes(shape: lr_block_shape, is_bwd: bool) -> int:
     return int(_lib.load().lr_block_workspace_bytes(ctypes.byref(shape), int(bool(is_bwd))))
+
+
+def workspace_tensor(shape: lr_block_shape, ws: torch.Tensor, is_bwd: bool, which: int):
+    """View of the d-wide intermediate `which` (LR_WS_H or LR_WS_M) inside a
+    block workspace (lr_block_workspace_tensor), as a [T, width] tensor."""
+    off, nb = ctypes.c_size_t(), ctypes.c_size_t()
+    _lib.check(_lib.load().lr_block_workspace_tensor(ctypes.byref(shape), int(bool(is_bwd)),
+                                                     int(which), ctypes.byref(off),
+                                                     ctypes.byref(nb)))
+    dt = torch_dtype(shape.dtype)
+    width = shape.d if which == _lib.LR_WS_H else shape.d_ff
+    raw = ws[off.value:off.value + nb.value]
+    return raw.view(dt).view(shape.T, width)
 
 
 def alloc_workspace(shape: lr_block_shape, is_bwd: bool, device="cuda") -> torch.Tensor:
@@ -197,14 +210,21 @@ def profile_enable(on: bool = True) -> None:
     _lib.check(_lib.load().lr_profile_enable(int(bool(on))))
 
 
-def profile_collect(max_kernels: int = 64) -> list[tuple[str, int, float]]:
-    """Wait for the recorded events; return [(kernel, launches, total ms)]."""
+def profile_repeat(n: int) -> None:
+    """While recording, enqueue each memory-bound launch n times between its events."""
+    _lib.check(_lib.load().lr_profile_repeat(int(n)))
+
+
+def profile_collect(max_kernels: int = 64, with_bytes: bool = False) -> list[tuple]:
+    """Wait for the recorded events; return [(kernel, launches, total ms)], with
+    ``with_bytes`` [(kernel, launches, total ms, algorithmic HBM bytes)]."""
     lib = _lib.load()
     arr = (_lib.lr_kernel_time * max_kernels)()
     n = lib.lr_profile_collect(arr, max_kernels)
     if n < 0:
         _lib.check(n)
     return [(arr[i].name.decode(), int(arr[i].count), float(arr[i].total_ms))
+            + ((float(arr[i].bytes),) if with_bytes else ())
             for i in range(min(n, max_kernels))]
 
 

@@ -24,14 +24,16 @@ LR_F32, LR_BF16 = 0, 1
 LR_STAGE_ALL, LR_STAGE_PRE_ATTN, LR_STAGE_POST_ATTN = 0, 1, 2
 LR_LAYOUT_NT, LR_LAYOUT_NN, LR_LAYOUT_TN = 0, 1, 2
 LR_EPI_NONE, LR_EPI_ADD_RESIDUAL, LR_EPI_SWIGLU_PAIR, LR_EPI_ROW_SCALE = 0, 1, 2, 3
+LR_WS_H, LR_WS_M = 0, 1
 
 # Every function include/lr_block.h declares.
 EXPORTS = (
-    "lr_block_workspace_bytes", "lr_block_fwd", "lr_block_bwd",
+    "lr_block_workspace_bytes", "lr_block_workspace_tensor", "lr_block_fwd", "lr_block_bwd",
     "lr_grouped_lowrank_gemm", "lr_grouped_lowrank_gemm_workspace_bytes",
     "lr_grouped_lowrank_gemm_ws", "lr_online_rmsnorm_gemm_workspace_bytes",
     "lr_online_rmsnorm_gemm", "lr_attention_workspace_bytes", "lr_attention_fwd",
-    "lr_attention_bwd", "lr_profile_enable", "lr_profile_collect", "lr_last_error",
+    "lr_attention_bwd", "lr_profile_enable", "lr_profile_collect", "lr_profile_repeat",
+    "lr_last_error",
     "lr_version",
 )
 
@@ -69,7 +71,8 @@ class lr_attn_shape(ctypes.Structure):
 
 
 class lr_kernel_time(ctypes.Structure):
-    _fields_ = [("name", ctypes.c_char * 64), ("count", c_int32), ("total_ms", c_float)]
+    _fields_ = [("name", ctypes.c_char * 64), ("count", c_int32), ("total_ms", c_float),
+                ("bytes", ctypes.c_double)]
 
 
 class lr_gemm_pair(ctypes.Structure):
@@ -96,6 +99,9 @@ def load(path: str | None = None):
                        POINTER(lr_block_partials))
     lib.lr_block_workspace_bytes.argtypes = [S, c_int32]
     lib.lr_block_workspace_bytes.restype = c_size_t
+    lib.lr_block_workspace_tensor.argtypes = [S, c_int32, c_int32, POINTER(c_size_t),
+                                              POINTER(c_size_t)]
+    lib.lr_block_workspace_tensor.restype = c_int32
     lib.lr_block_fwd.argtypes = [S, W, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p, SV, PT, c_int32, c_void_p, c_size_t, c_void_p]
     lib.lr_block_fwd.restype = c_int32
@@ -133,6 +139,8 @@ def load(path: str | None = None):
     lib.lr_profile_enable.restype = c_int32
     lib.lr_profile_collect.argtypes = [POINTER(lr_kernel_time), c_int32]
     lib.lr_profile_collect.restype = c_int32
+    lib.lr_profile_repeat.argtypes = [c_int32]
+    lib.lr_profile_repeat.restype = c_int32
     lib.lr_last_error.argtypes = []
     lib.lr_last_error.restype = ctypes.c_char_p
     lib.lr_version.argtypes = []

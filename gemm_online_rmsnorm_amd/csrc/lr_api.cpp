@@ -49,8 +49,11 @@ int hip_fail(hipError_t e, const char* what) {
 struct ProfRec {
   const char* name;
   hipEvent_t a, b;
+  int reps;      // launches between the two events
+  double bytes;  // algorithmic HBM bytes of those launches (memory-bound kernels)
 };
 std::atomic<bool> g_prof_on{false};
+std::atomic<int> g_prof_repeat{1};
 std::mutex g_prof_mu;
 std::vector<ProfRec> g_prof;
 std::vector<hipEvent_t> g_prof_pool;
@@ -67,24 +70,43 @@ hipEvent_t prof_event() {
 }
 
 // Records a start event on construction and a stop event on destruction.
+// A memory-bound launch site passes its algorithmic bytes and marks itself
+// repeatable: while recording with a repeat count n, it enqueues its kernel
+// reps() = n times back to back between the events (such kernels only read
+// buffers they do not write, so the result is unchanged).
 struct ProfScope {
   hipStream_t s;
   size_t idx = SIZE_MAX;
-  ProfScope(const char* name, hipStream_t st) : s(st) {
+  int n = 1;
+  ProfScope(const char* name, hipStream_t st, double bytes = 0.0, bool repeatable = false)
+      : s(st) {
     if (!g_prof_on.load(std::memory_order_relaxed)) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    ProfRec r{name, prof_event(), prof_event()};
+    ProfRec r{name, prof_event(), prof_event(), 1, 0.0};
     if (!r.a || !r.b) return;
+    if (repeatable) n = g_prof_repeat.load(std::memory_order_relaxed);
+    r.reps = n;
+    r.bytes = bytes * n;
     (void)hipEventRecord(r.a, s);
     idx = g_prof.size();
     g_prof.push_back(r);
   }
+  int reps() const { return n; }
   ~ProfScope() {
     if (idx == SIZE_MAX) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     (void)hipEventRecord(g_prof[idx].b, s);
   }
 };
+
+// Enqueues a memory-bound launch reps() times (once unless the measurement
+// hook asks for repetitions).
+template <class F>
+hipError_t launch_rep(const ProfScope& ps, F launch) {
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < ps.reps() && e == hipSuccess; ++i) e = launch();
+  return e;
+}
 
 size_t elem_size(int dtype) { return dtype == LR_F32 ? 4 : 2; }
 int vec_elems(int dtype) { return dtype == LR_F32 ? 4 : 8; }
@@ -277,13 +299,30 @@ int gemm(int op, int dtype, const lr::GemmDesc& d, int groups, hipStream_t st,
   return LR_OK;
 }
 
-// One weight-gradient GEMM (split-K through the workspace when it pays).
-int wgrad(int dtype, const lr::GemmDesc& d, int groups, const BwdWs& W, hipStream_t st,
-          const char* what) {
-  ProfScope ps(what, st);
-  hipError_t e = lr::run_wgrad(dtype, d, groups, W.wpart, W.wpart_bytes, st);
-  if (e != hipSuccess) return hip_fail(e, what);
+// One weight-gradient GEMM (split-K through the workspace when it pays):
+// the GEMM, then, with more than one K-slice, the fixed-order sum of the
+// slices (recorded by the measurement hook as `sum_name`).
+int wgrad(int dtype, const lr::GemmDesc& d, int groups, void* part, size_t part_bytes,
+          hipStream_t st, const char* what, const char* sum_name) {
+  const int splits = lr::wgrad_splits(dtype, d, groups, part, part_bytes);
+  {
+    ProfScope ps(what, st);
+    hipError_t e = lr::run_wgrad_gemm(dtype, d, groups, splits, part, st);
+    if (e != hipSuccess) return hip_fail(e, what);
+  }
+  if (splits > 1) {
+    const double mn = (double)d.M * d.N;
+    const double bytes = groups * mn * 4.0 * (splits + 1) + (d.colscale ? 2.0 * d.N : 0.0);
+    ProfScope ps(sum_name, st, bytes, true);
+    hipError_t e = launch_rep(ps, [&] { return lr::run_wgrad_sum(d, groups, splits, part, st); });
+    if (e != hipSuccess) return hip_fail(e, sum_name);
+  }
   return LR_OK;
+}
+
+int wgrad(int dtype, const lr::GemmDesc& d, int groups, const BwdWs& W, hipStream_t st,
+          const char* what, const char* sum_name) {
+  return wgrad(dtype, d, groups, W.wpart, W.wpart_bytes, st, what, sum_name);
 }
 
 #define RUN(x)            \
@@ -485,6 +524,12 @@ int lr_profile_enable(int32_t on) {
   return LR_OK;
 }
 
+int lr_profile_repeat(int32_t n) {
+  if (n < 1 || n > 1000) return fail(LR_ERR_INVALID_ARG, "repeat count %d is out of range [1, 1000]", n);
+  g_prof_repeat.store(n);
+  return LR_OK;
+}
+
 int lr_profile_collect(lr_kernel_time* out, int32_t max) {
   if (max < 0 || (max > 0 && !out)) return fail(LR_ERR_INVALID_ARG, "bad output array");
   std::lock_guard<std::mutex> lk(g_prof_mu);
@@ -492,6 +537,7 @@ int lr_profile_collect(lr_kernel_time* out, int32_t max) {
     const char* name;
     int count;
     double ms;
+    double bytes;
   };
   std::vector<Agg> agg;
   for (auto& r : g_prof) {
@@ -502,9 +548,10 @@ int lr_profile_collect(lr_kernel_time* out, int32_t max) {
     if (e != hipSuccess) return hip_fail(e, "profile elapsed time");
     size_t i = 0;
     while (i < agg.size() && std::strcmp(agg[i].name, r.name) != 0) ++i;
-    if (i == agg.size()) agg.push_back({r.name, 0, 0.0});
-    agg[i].count += 1;
+    if (i == agg.size()) agg.push_back({r.name, 0, 0.0, 0.0});
+    agg[i].count += r.reps;
     agg[i].ms += ms;
+    agg[i].bytes += r.bytes;
     g_prof_pool.push_back(r.a);
     g_prof_pool.push_back(r.b);
   }
@@ -513,6 +560,7 @@ int lr_profile_collect(lr_kernel_time* out, int32_t max) {
     std::snprintf(out[i].name, sizeof(out[i].name), "%s", agg[i].name);
     out[i].count = agg[i].count;
     out[i].total_ms = (float)agg[i].ms;
+    out[i].bytes = agg[i].bytes;
   }
   return (int)agg.size();
 }
@@ -520,6 +568,31 @@ int lr_profile_collect(lr_kernel_time* out, int32_t max) {
 size_t lr_block_workspace_bytes(const lr_block_shape* shape, int is_bwd) {
   if (check_shape(shape)) return 0;
   return is_bwd ? carve_bwd(shape, nullptr, nullptr) : carve_fwd(shape, nullptr, nullptr);
+}
+
+int lr_block_workspace_tensor(const lr_block_shape* shape, int32_t is_bwd, int32_t which,
+                              size_t* offset, size_t* bytes) {
+  RUN(check_shape(shape));
+  if (which != LR_WS_H && which != LR_WS_M)
+    return fail(LR_ERR_INVALID_ARG, "which = %d is not an lr_ws_tensor", which);
+  if (!offset || !bytes) return fail(LR_ERR_INVALID_ARG, "offset or bytes is NULL");
+  // Carved from a base of 256 (a null base carves sizes only), so that a
+  // region at offset 0 is told apart from a missing one.
+  void* const base = reinterpret_cast<void*>(uintptr_t(256));
+  const size_t e = elem_size(shape->dtype);
+  void* p;
+  if (is_bwd) {
+    BwdWs W;
+    carve_bwd(shape, base, &W);
+    p = which == LR_WS_H ? W.h : W.m;
+  } else {
+    FwdWs W;
+    carve_fwd(shape, base, &W);
+    p = which == LR_WS_H ? W.h : W.m;
+  }
+  *offset = reinterpret_cast<uintptr_t>(p) - 256;
+  *bytes = e * (size_t)shape->T * (size_t)(which == LR_WS_H ? shape->d : shape->d_ff);
+  return LR_OK;
 }
 
 int lr_block_fwd(const lr_block_shape* s, const lr_block_weights* w, const void* X,
@@ -572,8 +645,10 @@ int lr_block_fwd(const lr_block_shape* s, const lr_block_weights* w, const void*
     // Online RMSNorm + grouped [A_q; A_k; A_v] down-projection.
     hipError_t he;
     {
-      ProfScope ps("fold gamma1", st);
-      he = lr::run_fold_gamma(dt, w->A_qkv, d, w->gamma1, W.Ag_qkv, 3 * r, d, st);
+      ProfScope ps("fold gamma1", st, (double)e * (2.0 * 3 * r * d + d), true);
+      he = launch_rep(ps, [&] {
+        return lr::run_fold_gamma(dt, w->A_qkv, d, w->gamma1, W.Ag_qkv, 3 * r, d, st);
+      });
     }
     if (he != hipSuccess) return hip_fail(he, "fold gamma1");
     lr::GemmDesc g;
@@ -595,9 +670,11 @@ int lr_block_fwd(const lr_block_shape* s, const lr_block_weights* w, const void*
     g.emit_partial = part;
     RUN(gemm(lr::OP_NT_ORMS, dt, g, 1, st, "QKV Online RMSNorm GEMM"));
     if (part) {
-      ProfScope ps("QKV finalize", st);
-      he = lr::run_finalize(dt, pt->P_qkv, 3 * r, pt->ss1, T, 3 * r, inv_D, s->eps, sv->qkv_r,
-                            3 * r, sv->rms1, st);
+      ProfScope ps("QKV finalize", st, (double)e * 2.0 * T * 3 * r + 8.0 * T, true);
+      he = launch_rep(ps, [&] {
+        return lr::run_finalize(dt, pt->P_qkv, 3 * r, pt->ss1, T, 3 * r, inv_D, s->eps,
+                                sv->qkv_r, 3 * r, sv->rms1, st);
+      });
       if (he != hipSuccess) return hip_fail(he, "QKV finalize");
     }
     // Grouped Q, K, V up-projections: three (input, weight) pairs.
@@ -648,8 +725,10 @@ int lr_block_fwd(const lr_block_shape* s, const lr_block_weights* w, const void*
     // Online RMSNorm + grouped [A_g; A_u] down-projection.
     hipError_t he;
     {
-      ProfScope ps("fold gamma2", st);
-      he = lr::run_fold_gamma(dt, w->A_gu, d, w->gamma2, W.Ag_gu, 2 * r, d, st);
+      ProfScope ps("fold gamma2", st, (double)e * (2.0 * 2 * r * d + d), true);
+      he = launch_rep(ps, [&] {
+        return lr::run_fold_gamma(dt, w->A_gu, d, w->gamma2, W.Ag_gu, 2 * r, d, st);
+      });
     }
     if (he != hipSuccess) return hip_fail(he, "fold gamma2");
     lr::GemmDesc n2;
@@ -671,9 +750,11 @@ int lr_block_fwd(const lr_block_shape* s, const lr_block_weights* w, const void*
     n2.emit_partial = part;
     RUN(gemm(lr::OP_NT_ORMS, dt, n2, 1, st, "gate/up Online RMSNorm GEMM"));
     if (part) {
-      ProfScope ps("gate/up finalize", st);
-      he = lr::run_finalize(dt, pt->P_gu, 2 * r, pt->ss2, T, 2 * r, inv_D, s->eps, sv->gu_r,
-                            2 * r, sv->rms2, st);
+      ProfScope ps("gate/up finalize", st, (double)e * 2.0 * T * 2 * r + 8.0 * T, true);
+      he = launch_rep(ps, [&] {
+        return lr::run_finalize(dt, pt->P_gu, 2 * r, pt->ss2, T, 2 * r, inv_D, s->eps,
+                                sv->gu_r, 2 * r, sv->rms2, st);
+      });
       if (he != hipSuccess) return hip_fail(he, "gate/up finalize");
     }
     // m = SiLU(g_r B_g^T) * (u_r B_u^T), both pairs in one tile.
@@ -783,7 +864,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.ldb[0] = r;
       g.c[0] = gr->B_dn;
       g.ldc[0] = r;
-      RUN(wgrad(dt, g, 1, W, st, "dB_dn"));
+      RUN(wgrad(dt, g, 1, W, st, "dB_dn", "dB_dn split-K sum"));
     }
     // dd_r = dY B_dn
     {
@@ -861,7 +942,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.ldb[0] = F;
       g.c[0] = gr->A_dn;
       g.ldc[0] = F;
-      RUN(wgrad(dt, g, 1, W, st, "dA_dn"));
+      RUN(wgrad(dt, g, 1, W, st, "dA_dn", "dA_dn split-K sum"));
     }
     // dB_g = dg^T g_r, dB_u = du^T u_r (grouped)
     {
@@ -881,7 +962,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.ldb[1] = 2 * r;
       g.c[1] = gr->B_u;
       g.ldc[1] = r;
-      RUN(wgrad(dt, g, 2, W, st, "dB_g, dB_u"));
+      RUN(wgrad(dt, g, 2, W, st, "dB_g, dB_u", "dB_g, dB_u split-K sum"));
     }
     // dgus = [dg B_g | du B_u] / rms2 (grouped, row-scaled)
     {
@@ -906,9 +987,11 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
     }
     // coef2 = (dgus . gu_r) / (rms2 D)
     {
-      ProfScope ps("row dot 2", st);
-      hipError_t he = lr::run_rowdot_coef(dt, W.dgus, 2 * r, sv->gu_r, 2 * r, 2 * r, sv->rms2,
-                                          inv_D, W.coef2, T, st);
+      ProfScope ps("row dot 2", st, (double)e * 2.0 * T * 2 * r + 8.0 * T, true);
+      hipError_t he = launch_rep(ps, [&] {
+        return lr::run_rowdot_coef(dt, W.dgus, 2 * r, sv->gu_r, 2 * r, 2 * r, sv->rms2, inv_D,
+                                   W.coef2, T, st);
+      });
       if (he != hipSuccess) return hip_fail(he, "row dot 2");
     }
     // Recompute h = X + o_r B_o^T.
@@ -948,8 +1031,10 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.colsum = W.colpart;
       RUN(gemm(lr::OP_NN_RMSBWD, dt, g, 1, st, "RMSNorm-2 backward"));
       const int bm = lr::gemm_tile_m_used(lr::OP_NN_RMSBWD, dt, g, 1);
-      ProfScope ps("dgamma2 column sum", st);
-      hipError_t he = lr::run_colsum(W.colpart, (T + bm - 1) / bm, d, gr->gamma2, st);
+      const int tiles = (T + bm - 1) / bm;
+      ProfScope ps("dgamma2 column sum", st, 4.0 * tiles * d + 4.0 * d, true);
+      hipError_t he =
+          launch_rep(ps, [&] { return lr::run_colsum(W.colpart, tiles, d, gr->gamma2, st); });
       if (he != hipSuccess) return hip_fail(he, "dgamma2");
     }
     // dA_gu = gamma2 * (dgus^T h)
@@ -965,7 +1050,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.c[0] = gr->A_gu;
       g.ldc[0] = d;
       g.colscale = w->gamma2;
-      RUN(wgrad(dt, g, 1, W, st, "dA_gu"));
+      RUN(wgrad(dt, g, 1, W, st, "dA_gu", "dA_gu split-K sum"));
     }
     // dB_o = dh^T o_r
     {
@@ -979,7 +1064,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.ldb[0] = r;
       g.c[0] = gr->B_o;
       g.ldc[0] = r;
-      RUN(wgrad(dt, g, 1, W, st, "dB_o"));
+      RUN(wgrad(dt, g, 1, W, st, "dB_o", "dB_o split-K sum"));
     }
     // do_r = dh B_o
     {
@@ -1007,7 +1092,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.ldb[0] = d;
       g.c[0] = gr->A_o;
       g.ldc[0] = d;
-      RUN(wgrad(dt, g, 1, W, st, "dA_o"));
+      RUN(wgrad(dt, g, 1, W, st, "dA_o", "dA_o split-K sum"));
     }
     // dO = do_r A_o
     {
@@ -1043,7 +1128,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
         g.c[i] = dBs[i];
         g.ldc[i] = r;
       }
-      RUN(wgrad(dt, g, 3, W, st, "dB_q, dB_k, dB_v"));
+      RUN(wgrad(dt, g, 3, W, st, "dB_q, dB_k, dB_v", "dB_q, dB_k, dB_v split-K sum"));
     }
     // dqs = [dQ B_q | dK B_k | dV B_v] / rms1 (grouped, row-scaled)
     {
@@ -1064,9 +1149,11 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
     }
     // coef1 = (dqs . qkv_r) / (rms1 D)
     {
-      ProfScope ps("row dot 1", st);
-      hipError_t he = lr::run_rowdot_coef(dt, W.dqs, 3 * r, sv->qkv_r, 3 * r, 3 * r, sv->rms1,
-                                          inv_D, W.coef1, T, st);
+      ProfScope ps("row dot 1", st, (double)e * 2.0 * T * 3 * r + 8.0 * T, true);
+      hipError_t he = launch_rep(ps, [&] {
+        return lr::run_rowdot_coef(dt, W.dqs, 3 * r, sv->qkv_r, 3 * r, 3 * r, sv->rms1, inv_D,
+                                   W.coef1, T, st);
+      });
       if (he != hipSuccess) return hip_fail(he, "row dot 1");
     }
     // dX = dh + gamma1 * (dqs A_qkv) - coef1 * X; dgamma1 partials.
@@ -1090,8 +1177,10 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.colsum = W.colpart;
       RUN(gemm(lr::OP_NN_RMSBWD, dt, g, 1, st, "RMSNorm-1 backward"));
       const int bm = lr::gemm_tile_m_used(lr::OP_NN_RMSBWD, dt, g, 1);
-      ProfScope ps("dgamma1 column sum", st);
-      hipError_t he = lr::run_colsum(W.colpart, (T + bm - 1) / bm, d, gr->gamma1, st);
+      const int tiles = (T + bm - 1) / bm;
+      ProfScope ps("dgamma1 column sum", st, 4.0 * tiles * d + 4.0 * d, true);
+      hipError_t he =
+          launch_rep(ps, [&] { return lr::run_colsum(W.colpart, tiles, d, gr->gamma1, st); });
       if (he != hipSuccess) return hip_fail(he, "dgamma1");
     }
     // dA_qkv = gamma1 * (dqs^T X)
@@ -1107,7 +1196,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.c[0] = gr->A_qkv;
       g.ldc[0] = d;
       g.colscale = w->gamma1;
-      RUN(wgrad(dt, g, 1, W, st, "dA_qkv"));
+      RUN(wgrad(dt, g, 1, W, st, "dA_qkv", "dA_qkv split-K sum"));
     }
   }
   return LR_OK;
@@ -1146,10 +1235,8 @@ int lr_grouped_lowrank_gemm_ws(int32_t G, const lr_gemm_pair* pairs, int32_t dty
   const size_t need = op == lr::OP_TN_WGRAD ? lr::wgrad_part_bytes(dtype, g, groups) : 0;
   if (need == 0) return gemm(op, dtype, g, groups, st, "grouped low-rank GEMM");
   RUN(check_ws(ws, ws_bytes, need));
-  ProfScope ps("grouped low-rank GEMM", st);
-  hipError_t e = lr::run_wgrad(dtype, g, groups, ws, ws_bytes, st);
-  if (e != hipSuccess) return hip_fail(e, "grouped low-rank GEMM");
-  return LR_OK;
+  return wgrad(dtype, g, groups, ws, ws_bytes, st, "grouped low-rank GEMM",
+               "grouped low-rank GEMM split-K sum");
 }
 
 namespace {
@@ -1281,7 +1368,9 @@ int lr_online_rmsnorm_gemm(int64_t T, int64_t d, int64_t N, int32_t n_panels, in
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (gamma) {
-    hipError_t he = lr::run_fold_gamma(dtype, A, lda, gamma, ws, (int)N, (int)d, st);
+    ProfScope ps("fold gamma", st, (double)elem_size(dtype) * (2.0 * N * d + d), true);
+    hipError_t he = launch_rep(
+        ps, [&] { return lr::run_fold_gamma(dtype, A, lda, gamma, ws, (int)N, (int)d, st); });
     if (he != hipSuccess) return hip_fail(he, "fold gamma");
     Aeff = ws;
     ldaeff = d;

@@ -59,20 +59,24 @@ hipError_t run_gemm(int op, int dtype, const GemmDesc& d, int groups, hipStream_
 // it then uses (the RMSNorm-backward column partials have one row per M-tile).
 bool uses_engine2(int op, int dtype, const GemmDesc& d, int groups);
 int gemm2_tile_m(int op, const GemmDesc& d, int groups);
-void set_engine2(bool on);
 // M-tile of the kernel run_gemm dispatches for this call.
 int gemm_tile_m_used(int op, int dtype, const GemmDesc& d, int groups);
 // Smallest M-tile any GEMM kernel uses (sizes per-M-tile workspaces).
 constexpr int kMinTileM = 64;
 
 // Weight-gradient (TN) GEMM with deterministic split-K: when the output grid
-// is too small to fill the chip, K is cut into slices whose fp32 partials go
-// to `part` (part_bytes long) and are then added in a fixed order, with the
-// column scale applied, into d.c[slot]. Without split the GEMM writes d.c
-// directly. wgrad_part_bytes gives the partial workspace a call needs.
+// is too small to fill the chip, K is cut into `splits` slices whose fp32
+// partials go to `part` (run_wgrad_gemm); run_wgrad_sum then adds them in a
+// fixed order, with the column scale applied, into d.c[slot]. With one slice
+// the GEMM writes d.c directly and no sum is needed. wgrad_part_bytes gives
+// the partial workspace a call needs; wgrad_splits the slice count a call
+// with `part_bytes` of workspace at `part` runs with (1 without enough).
 size_t wgrad_part_bytes(int dtype, const GemmDesc& d, int groups);
-hipError_t run_wgrad(int dtype, const GemmDesc& d, int groups, void* part, size_t part_bytes,
-                     hipStream_t s);
+int wgrad_splits(int dtype, const GemmDesc& d, int groups, const void* part, size_t part_bytes);
+hipError_t run_wgrad_gemm(int dtype, const GemmDesc& d, int groups, int splits, void* part,
+                          hipStream_t s);
+hipError_t run_wgrad_sum(const GemmDesc& d, int groups, int splits, const void* part,
+                         hipStream_t s);
 
 // Memory-bound helpers.
 hipError_t run_fold_gamma(int dtype, const void* A, int64_t lda, const void* gamma, void* out,

@@ -323,10 +323,6 @@ static int engine2_bk(int op) {
   return (op == OP_NT_SWIGLU || op == OP_SWIGLU_BWD || op == OP_SWIGLU_BWD2) ? 32 : 64;
 }
 
-static bool g_engine2 = true;
-
-void set_engine2(bool on) { g_engine2 = on; }
-
 int gemm2_tile_m(int op, const GemmDesc& d, int groups) {
   if (op == OP_NT_SWIGLU || op == OP_SWIGLU_BWD2) {
     const int t = split_tile(d);
@@ -337,7 +333,7 @@ int gemm2_tile_m(int op, const GemmDesc& d, int groups) {
 }
 
 bool uses_engine2(int op, int dtype, const GemmDesc& d, int groups) {
-  return g_engine2 && dtype == 1 && eligible2(op, d, groups, engine2_bk(op));
+  return dtype == 1 && eligible2(op, d, groups, engine2_bk(op));
 }
 
 int gemm_tile_m_used(int op, int dtype, const GemmDesc& d, int groups) {
@@ -375,13 +371,17 @@ size_t wgrad_part_bytes(int dtype, const GemmDesc& d, int groups) {
   return (size_t)sp * groups * (size_t)d.M * d.N * sizeof(float);
 }
 
-hipError_t run_wgrad(int dtype, const GemmDesc& d, int groups, void* part, size_t part_bytes,
-                     hipStream_t s) {
+int wgrad_splits(int dtype, const GemmDesc& d, int groups, const void* part, size_t part_bytes) {
   const size_t need = wgrad_part_bytes(dtype, d, groups);
-  if (need == 0 || part == nullptr || part_bytes < need || d.N % 4 != 0)
-    return run_gemm(OP_TN_WGRAD, dtype, d, groups, s);
+  if (need == 0 || part == nullptr || part_bytes < need || d.N % 4 != 0) return 1;
+  return wgrad_split(d, groups);
+}
+
+hipError_t run_wgrad_gemm(int dtype, const GemmDesc& d, int groups, int splits, void* part,
+                          hipStream_t s) {
+  if (splits <= 1) return run_gemm(OP_TN_WGRAD, dtype, d, groups, s);
   GemmDesc q = d;
-  q.ksplit = wgrad_split(d, groups);
+  q.ksplit = splits;
   const int64_t mn = (int64_t)d.M * d.N;
   q.c_split_stride = groups * mn;
   q.colscale = nullptr;
@@ -390,16 +390,20 @@ hipError_t run_wgrad(int dtype, const GemmDesc& d, int groups, void* part, size_
     q.c[gidx] = pbase + gidx * mn;
     q.ldc[gidx] = d.N;
   }
-  hipError_t e = run_gemm2(OP_TN_WGRAD, q, groups, s);
-  if (e != hipSuccess) return e;
+  return run_gemm2(OP_TN_WGRAD, q, groups, s);
+}
+
+hipError_t run_wgrad_sum(const GemmDesc& d, int groups, int splits, const void* part,
+                         hipStream_t s) {
+  const int64_t mn = (int64_t)d.M * d.N;
+  const float* pbase = static_cast<const float*>(part);
   for (int gidx = 0; gidx < groups; ++gidx) {
     const int64_t nq = mn / 4;
     int grid = (int)std::min<int64_t>((nq + 255) / 256, 8192);
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, s, pbase + gidx * mn,
-                       q.ksplit, q.c_split_stride, mn, d.N,
-                       static_cast<const bf16_t*>(d.colscale), static_cast<float*>(d.c[gidx]),
-                       d.ldc[gidx]);
-    e = hipGetLastError();
+                       splits, groups * mn, mn, d.N, static_cast<const bf16_t*>(d.colscale),
+                       static_cast<float*>(d.c[gidx]), d.ldc[gidx]);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -68,6 +68,12 @@ def kernel_work(T: int, d: int, r: int, F: int, elem: int = 2, partials: bool = 
     return W
 
 
-# Kernels bounded by HBM bandwidth rather than by the matrix cores.
+# Kernels bounded by HBM bandwidth rather than by the matrix cores (the
+# fixed-order sums of split-K weight-gradient slices are named
+# "<weight gradient> split-K sum").
 MEMORY_BOUND = ("fold gamma1", "fold gamma2", "QKV finalize", "gate/up finalize",
                 "row dot 1", "row dot 2", "dgamma1 column sum", "dgamma2 column sum")
+
+
+def is_memory_bound(name: str) -> bool:
+    return name in MEMORY_BOUND or name.endswith("split-K sum")

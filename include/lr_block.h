@@ -152,6 +152,21 @@ typedef struct {
  * needs for this shape; 0 if the shape is invalid. */
 size_t lr_block_workspace_bytes(const lr_block_shape* shape, int is_bwd);
 
+/* Where a d-wide intermediate of the checkpointed stack sits in a block
+ * workspace, for callers that check the low-rank activation checkpointing
+ * (project page, "Three supporting changes": the backward recomputes the
+ * d-wide activations from the saved r-wide ones instead of storing them).
+ * which = LR_WS_H: h = X + o_r B_o^T [T, d]; LR_WS_M: m = SiLU(g) * u
+ * [T, d_ff]; both row-major in `dtype`. After lr_block_fwd with ALL or
+ * POST_ATTN the forward workspace (is_bwd = 0) holds the values the forward
+ * computed; after lr_block_bwd with ALL or POST_ATTN the backward workspace
+ * (is_bwd = 1) holds the values the backward recomputed. Writes the byte
+ * offset from the workspace start and the byte size; returns
+ * LR_ERR_INVALID_ARG for an invalid shape, `which` or a NULL output. */
+typedef enum { LR_WS_H = 0, LR_WS_M = 1 } lr_ws_tensor;
+int lr_block_workspace_tensor(const lr_block_shape* shape, int32_t is_bwd, int32_t which,
+                              size_t* offset, size_t* bytes);
+
 /* Forward pass (BOOST project page, "Three supporting changes"; the chunk
  * layout of "Move the chunk boundary to the bottleneck").
  *   X [T, d]        block input (residual stream), must stay unchanged
@@ -336,18 +351,32 @@ int lr_attention_bwd(const lr_attn_shape* shape, const void* Q, const void* K, c
  * (events are created on first use and reused; no device memory is
  * allocated). lr_profile_enable(1) starts a new recording, (0) stops it.
  * lr_profile_collect waits for the recorded events, writes up to `max`
- * per-kernel aggregates (name, launch count, summed milliseconds) in order
- * of first launch, clears the recording and returns the number of distinct
- * kernels (which may exceed `max`). Not thread-safe against concurrent
+ * per-kernel aggregates in order of first launch, clears the recording and
+ * returns the number of distinct kernels (which may exceed `max`). Each
+ * aggregate holds the kernel's name, its launch count, the summed
+ * milliseconds between its events and, for the memory-bound kernels (gamma
+ * fold, rank-share finalize, row dots, split-K sums, column sums), the
+ * algorithmic HBM bytes of those launches (every input read once, every
+ * output written once; 0 for the GEMMs). Not thread-safe against concurrent
  * recording from several host threads. */
 typedef struct {
   char name[64];
   int32_t count;
   float total_ms;
+  double bytes;
 } lr_kernel_time;
 
 int lr_profile_enable(int32_t on);
 int lr_profile_collect(lr_kernel_time* out, int32_t max);
+
+/* While recording, enqueue each memory-bound launch n times back to back
+ * between its pair of events (1 <= n <= 1000; 1 at load). Those kernels
+ * only read buffers they do not write, so repeating them changes no result;
+ * total_ms / count then measures one launch on the GPU without most of the
+ * host-to-GPU launch latency a single launch between two events includes.
+ * count includes the repetitions. Returns LR_ERR_INVALID_ARG outside the
+ * range. */
+int lr_profile_repeat(int32_t n);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* lr_last_error(void);

@@ -161,6 +161,41 @@ def test_grouped_gemm_validation():
     assert lib.lr_grouped_lowrank_gemm(2, mixed, _lib.LR_BF16, 0, 0, None) == _lib.LR_ERR_UNSUPPORTED
 
 
+def test_grouped_epilogue_inputs_are_per_pair_but_shared():
+    """The epilogue's input (residual or row scale) travels in each pair; a
+    grouped call must give every pair the same one, and the residual
+    epilogue takes one pair."""
+    lib = _ensure_built()
+    P = _lib.lr_gemm_pair
+    rs = lambda aux: P(64, 64, 64, 0x1000, 64, 0x2000, 64, 0x3000, 64, aux, 0)
+    same = (P * 2)(rs(0x8000), rs(0x8000))
+    diff = (P * 2)(rs(0x8000), rs(0x9000))
+    f = lib.lr_grouped_lowrank_gemm
+    assert f(2, diff, _lib.LR_BF16, _lib.LR_LAYOUT_NT, _lib.LR_EPI_ROW_SCALE, None) == \
+        _lib.LR_ERR_UNSUPPORTED
+    assert b"shared" in lib.lr_last_error()
+    res = lambda: P(64, 64, 64, 0x1000, 64, 0x2000, 64, 0x3000, 64, 0x8000, 64)
+    two = (P * 2)(res(), res())
+    assert f(2, two, _lib.LR_BF16, _lib.LR_LAYOUT_NT, _lib.LR_EPI_ADD_RESIDUAL, None) == \
+        _lib.LR_ERR_UNSUPPORTED
+    # a missing row-scale input, and an epilogue on the TN layout
+    assert f(1, (P * 1)(rs(None)), _lib.LR_BF16, _lib.LR_LAYOUT_NT, _lib.LR_EPI_ROW_SCALE,
+             None) == _lib.LR_ERR_INVALID_ARG
+    assert f(1, (P * 1)(rs(0x8000)), _lib.LR_BF16, _lib.LR_LAYOUT_TN, _lib.LR_EPI_ROW_SCALE,
+             None) == _lib.LR_ERR_UNSUPPORTED
+    assert same  # (a shared row scale is valid; it is run by the GPU tests)
+
+
+def test_partials_struct_carries_the_two_norm_payloads():
+    """The rank-share partials are the two Online RMSNorm payloads and their
+    sums of squares; the other two chunks' payloads are o_r and d_r
+    themselves (the saved activations)."""
+    names = [f for f, _ in _lib.lr_block_partials._fields_]
+    assert names == ["P_qkv", "P_gu", "ss1", "ss2"]
+    text = open(HEADER).read()
+    assert "P_o" not in re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+
+
 def test_grouped_gemm_workspace_variant_validation():
     """The workspace variant validates like the plain call and checks the
     workspace before launching anything (weight-gradient shape whose grid is
@@ -205,6 +240,15 @@ def test_online_rmsnorm_gemm_validation():
     assert call(ldx=100) == _lib.LR_ERR_INVALID_ARG
     assert call(part=3) == _lib.LR_ERR_INVALID_ARG
     assert lib.lr_online_rmsnorm_gemm_workspace_bytes(64, 256, _lib.LR_BF16) == 64 * 256 * 2
+
+
+def test_profile_repeat_range():
+    lib = _ensure_built()
+    assert lib.lr_profile_repeat(0) == _lib.LR_ERR_INVALID_ARG
+    assert b"out of range" in lib.lr_last_error()
+    assert lib.lr_profile_repeat(1001) == _lib.LR_ERR_INVALID_ARG
+    assert lib.lr_profile_repeat(20) == _lib.LR_OK
+    assert lib.lr_profile_repeat(1) == _lib.LR_OK
 
 
 def test_version_string():
@@ -263,3 +307,31 @@ def test_attention_validation():
     assert bwd(ctypes.byref(ok), *ptrs, 0x100000, need_f, None) == _lib.LR_ERR_WORKSPACE
     ptrs[7] = 0  # dK
     assert bwd(ctypes.byref(ok), *ptrs, 0x100000, need_b, None) == _lib.LR_ERR_INVALID_ARG
+
+
+def test_workspace_tensor_locations():
+    """h and m lie inside their workspace, apart, with their sizes."""
+    lib = _ensure_built()
+    for dt, e in ((_lib.LR_F32, 4), (_lib.LR_BF16, 2)):
+        s = _shape(dtype=dt)
+        for is_bwd in (0, 1):
+            total = lib.lr_block_workspace_bytes(ctypes.byref(s), is_bwd)
+            spans = []
+            for which, width in ((_lib.LR_WS_H, 256), (_lib.LR_WS_M, 688)):
+                off, nb = ctypes.c_size_t(), ctypes.c_size_t()
+                assert lib.lr_block_workspace_tensor(ctypes.byref(s), is_bwd, which,
+                                                     ctypes.byref(off), ctypes.byref(nb)) == 0
+                assert nb.value == e * 256 * width
+                assert off.value % 256 == 0 and off.value + nb.value <= total
+                spans.append((off.value, off.value + nb.value))
+            (a0, a1), (b0, b1) = sorted(spans)
+            assert a1 <= b0
+    s = _shape()
+    off, nb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.lr_block_workspace_tensor(ctypes.byref(s), 0, 2, ctypes.byref(off),
+                                         ctypes.byref(nb)) == _lib.LR_ERR_INVALID_ARG
+    assert lib.lr_block_workspace_tensor(ctypes.byref(s), 0, 0, None, ctypes.byref(nb)) == \
+        _lib.LR_ERR_INVALID_ARG
+    bad = _shape(d=250)
+    assert lib.lr_block_workspace_tensor(ctypes.byref(bad), 0, 0, ctypes.byref(off),
+                                         ctypes.byref(nb)) == _lib.LR_ERR_INVALID_ARG

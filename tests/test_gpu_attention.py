@@ -1,9 +1,9 @@
 """Parity of the causal RoPE attention entry points (lr_attention_fwd,
 lr_attention_bwd) with the fp64 oracle (oracle/attention.py): whole outputs
 on small ragged shapes (multi-head, grouped-query, multi-query, one-token
-sequences), and one (sequence, head group) of the LLaMA-2-7B shape
-(4 x 4096 tokens, 32 heads of 128) computed in the launch configuration the
-benchmark times."""
+sequences), and at the LLaMA-2-7B shape (4 x 4096 tokens, 32 heads of 128)
+computed in the launch configuration the benchmark times: every head of one
+sequence and one head group of each other sequence."""
 from __future__ import annotations
 
 import numpy as np
@@ -97,31 +97,37 @@ def _slice(a, b, S, h0, nh):
     return a[b * S:(b + 1) * S, h0 * DH:(h0 + nh) * DH]
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("s", [synth.ATTN_7B, synth.ATTN_7B_GQA], ids=["mha", "gqa"])
-def test_full_size_sampled_head_group(s):
-    """Full LLaMA-2-7B shape; the oracle recomputes one sequence and one
-    key/value head with its query heads (the outputs of that group depend on
-    nothing else)."""
+def test_full_size_every_head_of_one_sequence_and_a_group_of_each_other(s):
+    """Full LLaMA-2-7B shape in the launch configuration the benchmark
+    times. The oracle recomputes every query and key/value head of the first
+    sequence, and one key/value head with its query heads of every other
+    sequence (a different head in each); the outputs of a (sequence, head
+    group) depend on nothing else. Every other output is checked finite."""
     torch = gpu_or_skip()
     say(f"[attention full] {s.name}")
     inp = synth.make_attn_inputs(s)
     got = _run(torch, s, inp)
     for name in ("O", "lse", "dQ", "dK", "dV"):
         assert np.all(np.isfinite(got[name])), name
-    b, hk = s.n_seq - 1, s.Hkv // 2 + 1
     grp = s.H // s.Hkv
     S = s.seq_len
-    q = _slice(inp["Q"], b, S, hk * grp, grp)
-    k = _slice(inp["K"], b, S, hk, 1)
-    v = _slice(inp["V"], b, S, hk, 1)
-    do = _slice(inp["dO"], b, S, hk * grp, grp)
-    args = (S, grp, 1, DH, s.base)
-    O, lse = oa.attention_forward(q, k, v, *args)
-    dQ, dK, dV = oa.attention_backward(q, k, v, do, *args)
-    acc = ErrAcc()
-    acc.add("O", _slice(got["O"], b, S, hk * grp, grp), O)
-    acc.add("lse", got["lse"][hk * grp:(hk + 1) * grp, b * S:(b + 1) * S], lse)
-    acc.add("dQ", _slice(got["dQ"], b, S, hk * grp, grp), dQ)
-    acc.add("dK", _slice(got["dK"], b, S, hk, 1), dK)
-    acc.add("dV", _slice(got["dV"], b, S, hk, 1), dV)
-    acc.check(BF16_TOL, s.name)
+    # (sequence, first kv head, kv heads): all of sequence 0, then one group
+    # of each other sequence
+    parts = [(0, 0, s.Hkv)] + [(b, (5 * b + 1) % s.Hkv, 1) for b in range(1, s.n_seq)]
+    for b, hk, nk in parts:
+        q = _slice(inp["Q"], b, S, hk * grp, nk * grp)
+        k = _slice(inp["K"], b, S, hk, nk)
+        v = _slice(inp["V"], b, S, hk, nk)
+        do = _slice(inp["dO"], b, S, hk * grp, nk * grp)
+        args = (S, nk * grp, nk, DH, s.base)
+        O, lse = oa.attention_forward(q, k, v, *args)
+        dQ, dK, dV = oa.attention_backward(q, k, v, do, *args)
+        acc = ErrAcc()
+        acc.add("O", _slice(got["O"], b, S, hk * grp, nk * grp), O)
+        acc.add("lse", got["lse"][hk * grp:(hk + nk) * grp, b * S:(b + 1) * S], lse)
+        acc.add("dQ", _slice(got["dQ"], b, S, hk * grp, nk * grp), dQ)
+        acc.add("dK", _slice(got["dK"], b, S, hk, nk), dK)
+        acc.add("dV", _slice(got["dV"], b, S, hk, nk), dV)
+        acc.check(BF16_TOL, f"{s.name} sequence {b} kv heads {hk}..{hk + nk - 1}")
