@@ -171,6 +171,20 @@ def online_rmsnorm_gemm(X, gamma, A, out, *, n_panels=1, d_norm=None, eps=1e-5, 
         _stream(stream, X.device)))
 
 
+def online_rmsnorm_gemm_noalloc(X, gamma, A, out, *, n_panels=1, d_norm=None, eps=1e-5,
+                                rms_out=None, ss_out=None, emit_partial=False,
+                                stream=None) -> None:
+    """lr_online_rmsnorm_gemm_noalloc: as online_rmsnorm_gemm, with the
+    library's built-in scratch instead of a workspace."""
+    lib = _lib.load()
+    T, d = X.shape
+    N = A.shape[0]
+    dtype = LR_F32 if X.dtype == torch.float32 else LR_BF16
+    _lib.check(lib.lr_online_rmsnorm_gemm_noalloc(
+        T, d, N, n_panels, d_norm or d, eps, _ptr(X), d, _ptr(gamma), _ptr(A), d, _ptr(out), N,
+        _ptr(rms_out), _ptr(ss_out), int(bool(emit_partial)), dtype, _stream(stream, X.device)))
+
+
 def attn_shape(T, seq_len, n_heads, n_kv_heads=None, head_dim=128, rope_base=10000.0,
                dtype=LR_BF16) -> _lib.lr_attn_shape:
     return _lib.lr_attn_shape(T, seq_len, n_heads, n_kv_heads or n_heads, head_dim, dtype,

@@ -31,7 +31,8 @@ EXPORTS = (
     "lr_block_workspace_bytes", "lr_block_workspace_tensor", "lr_block_fwd", "lr_block_bwd",
     "lr_grouped_lowrank_gemm", "lr_grouped_lowrank_gemm_workspace_bytes",
     "lr_grouped_lowrank_gemm_ws", "lr_online_rmsnorm_gemm_workspace_bytes",
-    "lr_online_rmsnorm_gemm", "lr_attention_workspace_bytes", "lr_attention_fwd",
+    "lr_online_rmsnorm_gemm", "lr_online_rmsnorm_gemm_noalloc",
+    "lr_online_rmsnorm_gemm_noalloc_max_bytes", "lr_attention_workspace_bytes", "lr_attention_fwd",
     "lr_attention_bwd", "lr_profile_enable", "lr_profile_collect", "lr_profile_repeat",
     "lr_last_error",
     "lr_version",
@@ -125,6 +126,12 @@ def load(path: str | None = None):
         c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
         c_size_t, c_void_p]
     lib.lr_online_rmsnorm_gemm.restype = c_int32
+    lib.lr_online_rmsnorm_gemm_noalloc.argtypes = [
+        c_int64, c_int64, c_int64, c_int32, c_int64, c_float, c_void_p, c_int64, c_void_p,
+        c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_int32, c_void_p]
+    lib.lr_online_rmsnorm_gemm_noalloc.restype = c_int32
+    lib.lr_online_rmsnorm_gemm_noalloc_max_bytes.argtypes = []
+    lib.lr_online_rmsnorm_gemm_noalloc_max_bytes.restype = c_size_t
     AS = POINTER(lr_attn_shape)
     lib.lr_attention_workspace_bytes.argtypes = [AS, c_int32]
     lib.lr_attention_workspace_bytes.restype = c_size_t

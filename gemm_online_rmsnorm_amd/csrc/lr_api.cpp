@@ -1324,11 +1324,12 @@ size_t lr_online_rmsnorm_gemm_workspace_bytes(int64_t N, int64_t d, int32_t dtyp
   return (size_t)N * (size_t)d * elem_size(dtype);
 }
 
-int lr_online_rmsnorm_gemm(int64_t T, int64_t d, int64_t N, int32_t n_panels, int64_t d_norm,
-                           float eps, const void* X, int64_t ldx, const void* gamma,
-                           const void* A, int64_t lda, void* out, int64_t ldo, float* rms_out,
-                           float* ss_out, int32_t emit_partial, int32_t dtype, void* ws,
-                           size_t ws_bytes, void* stream) {
+namespace {
+// Argument checks of the Online RMSNorm GEMM (no HIP call).
+int check_orms(int64_t T, int64_t d, int64_t N, int32_t n_panels, int64_t d_norm, float eps,
+               const void* X, int64_t ldx, const void* gamma, const void* A, int64_t lda,
+               void* out, int64_t ldo, float* rms_out, float* ss_out, int32_t emit_partial,
+               int32_t dtype) {
   if (dtype != LR_F32 && dtype != LR_BF16)
     return fail(LR_ERR_INVALID_ARG, "dtype %d is neither LR_F32 nor LR_BF16", dtype);
   if (T < 1 || d < 1 || N < 1 || d_norm < 1 || T > kMaxDim || d > kMaxDim || N > kMaxDim ||
@@ -1357,22 +1358,23 @@ int lr_online_rmsnorm_gemm(int64_t T, int64_t d, int64_t N, int32_t n_panels, in
     return fail(LR_ERR_INVALID_ARG, "rms_out is not 4-byte aligned");
   if (ss_out && (reinterpret_cast<uintptr_t>(ss_out) & 3u))
     return fail(LR_ERR_INVALID_ARG, "ss_out is not 4-byte aligned");
+  return LR_OK;
+}
+
+// The launches of the Online RMSNorm GEMM once its arguments are checked:
+// with gamma, the gamma-folded copy of A goes to `fold` (N x d elements).
+int run_orms(int64_t T, int64_t d, int64_t N, int32_t n_panels, int64_t d_norm, float eps,
+             const void* X, int64_t ldx, const void* gamma, const void* A, int64_t lda, void* out,
+             int64_t ldo, float* rms_out, float* ss_out, int32_t emit_partial, int32_t dtype,
+             void* fold, hipStream_t st) {
   const void* Aeff = A;
   int64_t ldaeff = lda;
   if (gamma) {
-    const size_t need = (size_t)N * (size_t)d * elem_size(dtype);
-    if (ws_bytes < need || !ws)
-      return fail(LR_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
-                  ws_bytes, need);
-    if (!aligned16(ws)) return fail(LR_ERR_WORKSPACE, "workspace is not 16-byte aligned");
-  }
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (gamma) {
     ProfScope ps("fold gamma", st, (double)elem_size(dtype) * (2.0 * N * d + d), true);
     hipError_t he = launch_rep(
-        ps, [&] { return lr::run_fold_gamma(dtype, A, lda, gamma, ws, (int)N, (int)d, st); });
+        ps, [&] { return lr::run_fold_gamma(dtype, A, lda, gamma, fold, (int)N, (int)d, st); });
     if (he != hipSuccess) return hip_fail(he, "fold gamma");
-    Aeff = ws;
+    Aeff = fold;
     ldaeff = d;
   }
   lr::GemmDesc g;
@@ -1393,6 +1395,81 @@ int lr_online_rmsnorm_gemm(int64_t T, int64_t d, int64_t N, int32_t n_panels, in
   g.eps = eps;
   g.emit_partial = emit_partial;
   return gemm(lr::OP_NT_ORMS, dtype, g, 1, st, "Online RMSNorm GEMM");
+}
+
+// Scratch of the no-allocation variant: the gamma-folded copy of A. Each
+// GPU the library runs on holds its own copy of this array until the
+// process ends. In host code `scratch` names a host-side stand-in, never
+// the device memory: the device address comes from hipGetSymbolAddress,
+// once per device, and only that address is passed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the
+// first call on that device).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(LR_ERR_UNSUPPORTED, "device %d is beyond the %d the library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(LR_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return LR_OK;
+}
+}  // namespace
+
+int lr_online_rmsnorm_gemm(int64_t T, int64_t d, int64_t N, int32_t n_panels, int64_t d_norm,
+                           float eps, const void* X, int64_t ldx, const void* gamma,
+                           const void* A, int64_t lda, void* out, int64_t ldo, float* rms_out,
+                           float* ss_out, int32_t emit_partial, int32_t dtype, void* ws,
+                           size_t ws_bytes, void* stream) {
+  RUN(check_orms(T, d, N, n_panels, d_norm, eps, X, ldx, gamma, A, lda, out, ldo, rms_out, ss_out,
+                 emit_partial, dtype));
+  if (gamma) {
+    const size_t need = (size_t)N * (size_t)d * elem_size(dtype);
+    if (ws_bytes < need || !ws)
+      return fail(LR_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                  ws_bytes, need);
+    if (!aligned16(ws)) return fail(LR_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+  }
+  return run_orms(T, d, N, n_panels, d_norm, eps, X, ldx, gamma, A, lda, out, ldo, rms_out, ss_out,
+                  emit_partial, dtype, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t lr_online_rmsnorm_gemm_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int lr_online_rmsnorm_gemm_noalloc(int64_t T, int64_t d, int64_t N, int32_t n_panels,
+                                   int64_t d_norm, float eps, const void* X, int64_t ldx,
+                                   const void* gamma, const void* A, int64_t lda, void* out,
+                                   int64_t ldo, float* rms_out, float* ss_out,
+                                   int32_t emit_partial, int32_t dtype, void* stream) {
+  RUN(check_orms(T, d, N, n_panels, d_norm, eps, X, ldx, gamma, A, lda, out, ldo, rms_out, ss_out,
+                 emit_partial, dtype));
+  void* fold = nullptr;
+  if (gamma) {
+    const size_t need = (size_t)N * (size_t)d * elem_size(dtype);
+    if (need > kScratchBytes)
+      return fail(LR_ERR_WORKSPACE,
+                  "the gamma-folded A (N x d = %lld x %lld) needs %zu bytes, more than the %zu "
+                  "bytes of built-in scratch of the no-allocation variant",
+                  (long long)N, (long long)d, need, kScratchBytes);
+    RUN(scratch_address(&fold));
+  }
+  return run_orms(T, d, N, n_panels, d_norm, eps, X, ldx, gamma, A, lda, out, ldo, rms_out, ss_out,
+                  emit_partial, dtype, fold, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -287,6 +287,26 @@ int lr_online_rmsnorm_gemm(int64_t T, int64_t d, int64_t N, int32_t n_panels, in
                            float* ss_out, int32_t emit_partial, int32_t dtype, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* The same Online RMSNorm GEMM without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). It allocates nothing and
+ * calls no allocating routine: the gamma-folded copy of A goes to a scratch
+ * array built into the library, lr_online_rmsnorm_gemm_noalloc_max_bytes()
+ * bytes (64 MiB) per GPU, held by each GPU the library runs on until the
+ * process ends. Arguments, outputs and errors are those of
+ * lr_online_rmsnorm_gemm; in addition, with gamma given, N * d elements of
+ * `dtype` beyond the scratch size return LR_ERR_WORKSPACE before anything
+ * is enqueued. The calling thread's current device must be the one `stream`
+ * belongs to. Every call on one GPU shares that GPU's scratch: calls that
+ * may overlap in time on one GPU (several streams or host threads) race,
+ * and the caller must order them. */
+size_t lr_online_rmsnorm_gemm_noalloc_max_bytes(void);
+int lr_online_rmsnorm_gemm_noalloc(int64_t T, int64_t d, int64_t N, int32_t n_panels,
+                                   int64_t d_norm, float eps, const void* X, int64_t ldx,
+                                   const void* gamma, const void* A, int64_t lda, void* out,
+                                   int64_t ldo, float* rms_out, float* ss_out,
+                                   int32_t emit_partial, int32_t dtype, void* stream);
+
 /* ------------------------------------------------------------------------
  * Causal self-attention with rotary position embedding (the attention core
  * the block's forward leaves between Q, K, V and O). The BOOST pages do not

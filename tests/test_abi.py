@@ -335,3 +335,31 @@ def test_workspace_tensor_locations():
     bad = _shape(d=250)
     assert lib.lr_block_workspace_tensor(ctypes.byref(bad), 0, 0, ctypes.byref(off),
                                          ctypes.byref(nb)) == _lib.LR_ERR_INVALID_ARG
+
+
+def test_online_rmsnorm_gemm_noalloc_validation():
+    """The no-allocation variant checks like the workspace variant and
+    rejects a gamma-folded A beyond its built-in scratch before any HIP
+    call (these run on a host without a GPU)."""
+    lib = _ensure_built()
+    f = lib.lr_online_rmsnorm_gemm_noalloc
+    cap = lib.lr_online_rmsnorm_gemm_noalloc_max_bytes()
+    assert cap == 64 << 20
+    ok = dict(T=64, d=256, N=64, P=1, D=256, eps=1e-5, X=0x1000, ldx=256, g=0x2000, A=0x3000,
+              lda=256, out=0x4000, ldo=64, rms=None, ss=None, part=0, dt=_lib.LR_BF16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["T"], a["d"], a["N"], a["P"], a["D"], a["eps"], a["X"], a["ldx"], a["g"],
+                 a["A"], a["lda"], a["out"], a["ldo"], a["rms"], a["ss"], a["part"], a["dt"], None)
+
+    assert call(P=3) == _lib.LR_ERR_INVALID_ARG
+    assert call(P=8) == _lib.LR_ERR_UNSUPPORTED
+    assert call(X=0x1001) == _lib.LR_ERR_INVALID_ARG
+    assert call(part=3) == _lib.LR_ERR_INVALID_ARG
+    # 8192 x 4104 bf16 is 64.1 MiB: one row past the scratch
+    assert call(N=8192, d=4104, ldx=4104, lda=4104, ldo=8192) == _lib.LR_ERR_WORKSPACE
+    assert b"scratch" in lib.lr_last_error()
+    assert call(N=4096, d=4104, ldx=4104, lda=4104, ldo=4096, dt=_lib.LR_F32) == \
+        _lib.LR_ERR_WORKSPACE
