@@ -48,11 +48,17 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 // pair 1's; waves of the first NWN / 2 columns multiply pair 0, the others
 // pair 1. Each wave runs one pair, so the LDS reads per MFMA are those of a
 // one-pair tile twice the size; the epilogue pairs up the two halves.
+// BDIAG_ = 1: a two-pair tile whose pairs share the output tile and run one
+// after the other along K (a block-diagonal product): the K loop multiplies
+// pair 0 (A0, B0) into the first accumulator set, then pair 1 into the
+// second, so every wave holds both results of its elements and a stage
+// holds one pair's A and B tiles.
 template <int BM_, int BN_, int BK_, int NWM_, int NWN_, int NSTAGE_, int NSPLIT_ = 1,
-          int NSTAGE_A_ = 0>
+          int NSTAGE_A_ = 0, int BDIAG_ = 0>
 struct Tile2 {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, NWM = NWM_, NWN = NWN_;
   static constexpr int NSTAGE = NSTAGE_;
+  static constexpr bool BDIAG = BDIAG_ != 0;
   // NSTAGE_A_ > 0: the A operand (the streamed activation of a one-pair
   // product) gets a ring of its own with NSTAGE_A_ stages and B keeps
   // NSTAGE, so A's loads are issued NSTAGE_A_ - 1 K-tiles ahead.
@@ -427,7 +433,8 @@ struct Opnd {
 
 template <class TL, int NPAIR>
 constexpr int stage_bytes() {
-  return (TL::NSPLIT == 2 ? 2 * TL::BM + TL::BN : NPAIR * (TL::BM + TL::BN)) * TL::BK * 2;
+  return (TL::NSPLIT == 2 ? 2 * TL::BM + TL::BN
+                          : (TL::BDIAG ? 1 : NPAIR) * (TL::BM + TL::BN)) * TL::BK * 2;
 }
 // The operand ring: NSTAGE stages, or with separate rings NSTAGE_A A tiles
 // followed by NSTAGE B tiles.
@@ -509,6 +516,10 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   constexpr bool SPLITN = (TL::NSPLIT == 2);
   static_assert(!SPLITN || (NPAIR == 2 && MCMASK == 0u && !ORMS && EPI != EPI_RMSBWD),
                 "split tiles are for K-contiguous two-pair products");
+  constexpr bool BD = TL::BDIAG;
+  static_assert(!BD || (NPAIR == 2 && MCMASK == 0u && !ORMS && !SPLITN && !TL::ASYM &&
+                        (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD2)),
+                "block-diagonal tiles are for the K-contiguous gate/up pair");
   constexpr int BNO = TL::BNO;
   constexpr int SB = stage_bytes<TL, NPAIR>();
   extern __shared__ __align__(16) unsigned char lds[];
@@ -547,7 +558,10 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   // which keep every wave issuing its share). Split tiles load 1.25 times
   // the bytes per MFMA: there the older waves stall behind their loads (the
   // younger ones then wait at the barrier for half the loop), and every
-  // wave issues its share (measured: 6-9% faster).
+  // wave issues its share (measured: 6-9% faster). Block-diagonal tiles,
+  // which load 1.5 times the bytes per MFMA of a one-pair 256 x 256 tile
+  // through three stages, are faster with the older half issuing (measured:
+  // all eight waves issuing made the SwiGLU tiles 3-5% slower).
   constexpr int NDMA = (TL::NWAVE == 8 && MCMASK == 0u && !SPLITN) ? TL::NWAVE / 2 : TL::NWAVE;
   using OA0 = Opnd<BM, BK, NDMA, !(MCMASK & 1u)>;
   using OB0 = Opnd<BNO, BK, NDMA, !(MCMASK & 2u)>;
@@ -639,6 +653,22 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     // without branches.
     const bool live = kt < g.ktiles_split;
     auto nb = [&](int64_t e, int64_t step) { return live ? (uint32_t)(2 * (e - kt * step)) : 0u; };
+    if constexpr (BD) {
+      // [A][B] of pair 0 for the first ktiles_split K-tiles, then of pair 1.
+      const int nkh = g.ktiles_split;
+      const bool second = kt >= nkh;
+      const int lk = second ? kt - nkh : kt;
+      const bool on = kt < 2 * nkh;
+      auto nbd = [&](int64_t e, int64_t step) { return on ? (uint32_t)(2 * (e - lk * step)) : 0u; };
+      if (!second) {
+        a0.issue(pa[0] + lk * sa[0], nbd(ea[0], sa[0]), st, wave);
+        b0.issue(pb[0] + lk * sb[0], nbd(eb[0], sb[0]), st + BM * BK * 2, wave);
+      } else {
+        a1.issue(pa[1] + lk * sa[1], nbd(ea[1], sa[1]), st, wave);
+        b1.issue(pb[1] + lk * sb[1], nbd(eb[1], sb[1]), st + BM * BK * 2, wave);
+      }
+      return;
+    }
     if constexpr (SPLITN) {
       // [A0][A1][B0][B1]: the two B tiles form one BN-row tile.
       a0.issue(pa[0] + kt * sa[0], nb(ea[0], sa[0]), st, wave);
@@ -658,8 +688,11 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       b2.issue(pb[2] + kt * sb[2], nb(eb[2], sb[2]), st + (3 * BM + 2 * BN) * BK * 2, wave);
     }
   };
-  constexpr int L = OA0::PER + OB0::PER + (NPAIR > 1 ? OA1::PER + OB1::PER : 0) +
-                    (NPAIR > 2 ? OA2::PER + OB2::PER : 0);
+  constexpr int L = BD ? OA0::PER + OB0::PER
+                      : OA0::PER + OB0::PER + (NPAIR > 1 ? OA1::PER + OB1::PER : 0) +
+                            (NPAIR > 2 ? OA2::PER + OB2::PER : 0);
+  static_assert(!BD || (OA0::PER == OA1::PER && OB0::PER == OB1::PER),
+                "both pairs of a block-diagonal tile load alike");
   static_assert(L * (S - 1) < 64, "too many loads in flight for vmcnt");
 
   constexpr int NACC = SPLITN ? 1 : NPAIR;
@@ -692,7 +725,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   // while the MFMAs of sub-step q run. The stage barrier sits before the
   // last sub-step of a K-tile, once its fragments are in registers, so the
   // first fragments of the next K-tile load under that sub-step's MFMAs.
-  constexpr int Q = (SPLITN ? 1 : NPAIR) * TL::NSTEP;
+  constexpr int Q = ((SPLITN || BD) ? 1 : NPAIR) * TL::NSTEP;
   u32x4 fa[2][FM], fb[2][FN];
   // st: the stage of K-tile kt (one ring); separate rings use kt.
   auto read_q = [&](int kt, const unsigned char* st, int q, int buf) {
@@ -730,8 +763,9 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
             tB, Opnd<BN, BK, TL::NWAVE, true>::frag_off(w0n + 16 * j, s, lane));
     }
   };
-  auto compute_q = [&](int q, int buf) {
-    const int p = q / TL::NSTEP;
+  // ph: the pair a block-diagonal tile's current K-tile belongs to.
+  auto compute_q = [&](int q, int buf, auto ph_tag) {
+    const int p = BD ? decltype(ph_tag)::value : q / TL::NSTEP;
     if constexpr (ORMS) {
       if (p == 0) {
 #pragma unroll
@@ -796,7 +830,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   // One K-tile. Fragment buffer of sub-step q of K-tile kt: (kt Q + q) & 1,
   // i.e. (q + B0) & 1 with B0 = (kt Q) & 1; with an odd sub-step count the
   // loop runs K-tiles in pairs so that B0 stays a constant.
-  auto ktile = [&](int kt, auto b0_tag) {
+  auto ktile = [&](int kt, auto b0_tag, auto ph_tag) {
     constexpr int B0 = decltype(b0_tag)::value;
     const unsigned char* st = stage_ptr(kt % S);
 #pragma unroll
@@ -810,7 +844,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       sched_fence();
       if (q + 1 < Q) {
         read_q(kt, st, q + 1, buf ^ 1);
-        compute_q(q, buf);
+        compute_q(q, buf, ph_tag);
         interleave<NDS, 0, FM * FN>();
       } else {
         // Every wave has its fragments of K-tile kt in registers once it
@@ -828,7 +862,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
           issue(kt + S);
         }
         read_q(kt + 1, stage_ptr((kt + 1) % S), 0, buf ^ 1);
-        compute_q(q, buf);
+        compute_q(q, buf, ph_tag);
         interleave<NDS, L, FM * FN>();
       }
     }
@@ -851,13 +885,20 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     wait_lgkmcnt0();
     sched_fence();
   };
-  if constexpr (Q & 1) {
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  if constexpr (BD) {
+    // nk K-tiles of pair 0, then nk of pair 1 (nk = ktiles_split each).
+    static_assert(!(Q & 1), "block-diagonal tiles take an even sub-step count");
+    for (int kt = 0; kt < nk; ++kt) ktile(kt, I0{}, I0{});
+    for (int kt = nk; kt < 2 * nk; ++kt) ktile(kt, I0{}, I1{});
+  } else if constexpr (Q & 1) {
     for (int kt = 0; kt < nk; kt += 2) {
-      ktile(kt, std::integral_constant<int, 0>{});
-      if (kt + 1 < nk) ktile(kt + 1, std::integral_constant<int, 1>{});
+      ktile(kt, I0{}, I0{});
+      if (kt + 1 < nk) ktile(kt + 1, I1{}, I0{});
     }
   } else {
-    for (int kt = 0; kt < nk; ++kt) ktile(kt, std::integral_constant<int, 0>{});
+    for (int kt = 0; kt < nk; ++kt) ktile(kt, I0{}, I0{});
   }
   // The last fragment reads (of a stage no MFMA uses, or before the loop
   // with no K-tile at all) and the empty-range loads past the last K-tile

@@ -129,6 +129,14 @@ using PS256x128 = Tile2<256, 256, 32, 2, 4, 3, 2>;
 // 64-byte row halves, which k-tiles of 32 give, copy at half the rate and
 // bound the 256-row tile.
 using PS192x128 = Tile2<192, 256, 64, 2, 4, 2, 2>;
+// Block-diagonal gate/up tile: 256 rows x 128 columns of both g and u, the
+// K loop running the gate pair and then the up pair; a stage is one pair's
+// A and B tiles (48 KB), so three stages fit, and every wave (64 x 64 of
+// both) combines g and u in registers without an exchange.
+using PBD256x128 = Tile2<256, 128, 64, 4, 2, 3, 1, 0, 1>;
+#ifndef LR_SWIGLU_TILE
+#define LR_SWIGLU_TILE 1
+#endif
 
 template <class TL, int NPAIR, uint32_t MC, int EPI>
 static hipError_t launch2(const GemmDesc& d, int groups, hipStream_t s) {
@@ -257,10 +265,12 @@ static hipError_t launch_single(const GemmDesc& d, int groups, hipStream_t s) {
   }
 }
 
-// Tile choice of the gate/up pair GEMMs: 0 the 192-row split tile (k-tiles
-// of 64), 1 the 256-row split tile (k-tiles of 32), 2 the 128 x 128 two-pair
-// tile for grids that would leave CUs idle.
+// Tile choice of the gate/up pair GEMMs: 3 the block-diagonal 256 x 128
+// tile, 0 the 192-row split tile (k-tiles of 64), 1 the 256-row split tile
+// (k-tiles of 32), 2 the 128 x 128 two-pair tile for grids that would leave
+// CUs idle.
 static int split_tile(const GemmDesc& d) {
+  if (LR_SWIGLU_TILE == 1 && d.K % 64 == 0 && ntiles(d, 256, 128, 1) >= kCUs) return 3;
   if (d.K % 64 == 0 && ntiles(d, 192, 128, 1) >= kCUs) return 0;
   if (ntiles(d, 256, 128, 1) >= kCUs) return 1;
   return 2;
@@ -304,6 +314,7 @@ static hipError_t run_gemm2(int op, const GemmDesc& d, int groups, hipStream_t s
     case OP_NN_RMSBWD: return launch_single<EPI_RMSBWD, 2u>(d, groups, s);
     case OP_NT_SWIGLU:
       switch (split_tile(d)) {
+        case 3: return launch2<PBD256x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
         case 0: return launch2<PS192x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
         case 1: return launch2<PS256x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
         default: return launch2<P2x128x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
@@ -311,6 +322,7 @@ static hipError_t run_gemm2(int op, const GemmDesc& d, int groups, hipStream_t s
     case OP_SWIGLU_BWD: return launch2<P3x128x128, 3, 32u, EPI_SWIGLU_BWD>(d, 1, s);
     case OP_SWIGLU_BWD2:
       switch (split_tile(d)) {
+        case 3: return launch2<PBD256x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
         case 0: return launch2<PS192x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
         case 1: return launch2<PS256x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
         default: return launch2<P2x128x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
@@ -326,7 +338,7 @@ static int engine2_bk(int op) {
 int gemm2_tile_m(int op, const GemmDesc& d, int groups) {
   if (op == OP_NT_SWIGLU || op == OP_SWIGLU_BWD2) {
     const int t = split_tile(d);
-    return t == 0 ? 192 : (t == 1 ? 256 : 128);
+    return t == 0 ? 192 : ((t == 1 || t == 3) ? 256 : 128);
   }
   if (op == OP_SWIGLU_BWD) return 128;
   return single_tile(d, groups) == 2 ? 128 : 256;
