@@ -495,14 +495,15 @@ constexpr int gemm2_body_bytes() {
   constexpr int epi = in_end > epi_area_bytes<TL>() ? in_end : epi_area_bytes<TL>();
   return ring > epi ? ring : epi;
 }
-// Per-panel row sums of squares and row scales of the Online RMSNorm.
-template <class TL, int EPI>
-constexpr int orms_bytes() {
-  return EPI == EPI_ORMS ? 8 * TL::BM * 4 + TL::BM * 4 : 0;
+// The Online RMSNorm's per-row totals and row scales (two floats per row)
+// live in the ring once the main loop is done, after the staging area.
+template <class TL>
+constexpr int orms_off() {
+  return (epi_area_bytes<TL>() + 1023) / 1024 * 1024;
 }
 template <class TL, int NPAIR, int EPI>
 constexpr int gemm2_lds_bytes() {
-  return gemm2_body_bytes<TL, NPAIR, EPI>() + orms_bytes<TL, EPI>();
+  return gemm2_body_bytes<TL, NPAIR, EPI>();
 }
 
 // ---------------------------------------------------------------------------
@@ -532,8 +533,10 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   constexpr int XCH = epi_xch_bytes<TL, EPI>();
   constexpr int IN0 = epi_in0<TL, EPI>();
   constexpr int BODY = gemm2_body_bytes<TL, NPAIR, EPI>();
-  float* sSS = reinterpret_cast<float*>(lds + BODY);  // [8][BM]
-  float* sRow = sSS + 8 * BM;                          // [BM]
+  // Online RMSNorm, after the main loop: per-row sums of squares, row scales.
+  float* sTot = reinterpret_cast<float*>(lds + orms_off<TL>());  // [BM]
+  float* sRow = sTot + BM;                                      // [BM]
+  static_assert(!ORMS || orms_off<TL>() + 8 * BM <= BODY, "row sums exceed the ring");
 
   // The wave index is uniform across a wave: keep it in a scalar register.
   const int tid = threadIdx.x, lane = tid & 63;
@@ -715,9 +718,15 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   // Online RMSNorm: the waves of one row band (same wm) read the same A
   // fragments; wave wn sums the squares of fragments i = wn, wn + NWN, ...
   constexpr int FSS = (FM + TL::NWN - 1) / TL::NWN;
-  float ssp[FSS];
+  // ssp: this lane's part of the current panel's sums; tot: the sums of the
+  // finished panels, added in panel order (lanes 0..15 hold rows 0..15 of
+  // the fragment after the cross-lane sums).
+  float ssp[FSS], tot[FSS];
 #pragma unroll
-  for (int i = 0; i < FSS; ++i) ssp[i] = 0.f;
+  for (int i = 0; i < FSS; ++i) ssp[i] = tot[i] = 0.f;
+  // Per-panel sums are written as each panel ends (by the first column tile
+  // of a row band only) unless the caller asked for the total.
+  const bool ss_panels = ORMS && g.ss_out != nullptr && !g.emit_partial && tn == 0;
   int panel = 0, in_panel = 0;
 
   // Fragment registers are double-buffered: the LDS reads of sub-step q + 1
@@ -874,7 +883,12 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
             float x = ssp[i / TL::NWN];
             x += __shfl_xor(x, 16, 64);
             x += __shfl_xor(x, 32, 64);
-            if (lane < 16) sSS[panel * BM + w0m + 16 * i + lane] = x;
+            tot[i / TL::NWN] += x;
+            const int gr = m0 + w0m + 16 * i + lane;
+            // One vector store among the ring's loads: a wait for at most n
+            // operations in flight then waits for one load more than it
+            // would have (operations retire in order), never for fewer.
+            if (ss_panels && lane < 16 && gr < M) g.ss_out[(int64_t)panel * M + gr] = x;
             ssp[i / TL::NWN] = 0.f;
           }
         ++panel;
@@ -908,7 +922,13 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   wait_lgkmcnt0();
   wait_vmcnt<0>();
   sched_fence();
-  __syncthreads();  // every wave is done with the ring; sSS is visible
+  __syncthreads();  // every wave is done with the ring
+  if constexpr (ORMS) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      if (i % TL::NWN == wn && lane < 16) sTot[w0m + 16 * i + lane] = tot[i / TL::NWN];
+    __syncthreads();
+  }
 
   // Epilogue geometry. Split tiles: the wave running pair 0 (gate) and its
   // partner in the same row band running pair 1 (up) each finish half of the
@@ -1003,20 +1023,14 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
 
   if constexpr (ORMS) {
     for (int r = tid; r < BM; r += TL::NT) {
-      float ss = 0.f;
-      for (int p = 0; p < g.n_panels; ++p) ss += sSS[p * BM + r];
+      const float ss = sTot[r];
       const float rmsg = sqrtf(ss * g.inv_D + g.eps);
       sRow[r] = g.emit_partial ? 1.0f : 1.0f / rmsg;
       const int gr = m0 + r;
       if (tn == 0 && gr < M) {
         if (g.rms_out && !g.emit_partial) g.rms_out[gr] = rmsg;
-        if (g.ss_out) {
-          if (g.emit_partial) {
-            g.ss_out[gr] = ss;
-          } else {
-            for (int p = 0; p < g.n_panels; ++p) g.ss_out[(int64_t)p * M + gr] = sSS[p * BM + r];
-          }
-        }
+        // (per-panel sums were written as their panels ended)
+        if (g.ss_out && g.emit_partial) g.ss_out[gr] = ss;
       }
     }
     __syncthreads();

@@ -114,7 +114,7 @@ static hipError_t dispatch(int op, const GemmDesc& d, int groups, hipStream_t s)
 // ---------------------------------------------------------------------------
 using P256x256 = Tile2<256, 256, 64, 2, 4, 2>;
 // The same tile with separate rings: 3 stages of the A tile, 2 of the B
-// tile (160 KB), for one-pair NT products without the Online RMSNorm sums.
+// tile (160 KB), for the one-pair NT products (Online RMSNorm included).
 using P256x256a = Tile2<256, 256, 64, 2, 4, 2, 1, 3>;
 using P256x128 = Tile2<256, 128, 64, 2, 2, 2>;
 using P128x128 = Tile2<128, 128, 64, 2, 2, 2>;
@@ -258,7 +258,7 @@ template <int EPI, uint32_t MC>
 static hipError_t launch_single(const GemmDesc& d, int groups, hipStream_t s) {
   switch (single_tile(d, groups)) {
     case 0:
-      if constexpr (EPI == EPI_ORMS || MC != 0u) return launch2<P256x256, 1, MC, EPI>(d, groups, s);
+      if constexpr (MC != 0u) return launch2<P256x256, 1, MC, EPI>(d, groups, s);
       else return launch2<P256x256a, 1, MC, EPI>(d, groups, s);
     case 1: return launch2<P256x128, 1, MC, EPI>(d, groups, s);
     default: return launch2<P128x128, 1, MC, EPI>(d, groups, s);
