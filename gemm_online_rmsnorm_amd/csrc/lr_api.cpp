@@ -851,6 +851,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float inv_D = 1.0f / (float)s->d_norm;
 
+  int cs_tiles = 0;  // M-tiles of the RMSNorm backward (rows of its column partials)
   if (post) {
     // dB_dn = dY^T d_r
     {
@@ -1031,13 +1032,11 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.colsum = W.colpart;
       RUN(gemm(lr::OP_NN_RMSBWD, dt, g, 1, st, "RMSNorm-2 backward"));
       const int bm = lr::gemm_tile_m_used(lr::OP_NN_RMSBWD, dt, g, 1);
-      const int tiles = (T + bm - 1) / bm;
-      ProfScope ps("dgamma2 column sum", st, 4.0 * tiles * d + 4.0 * d, true);
-      hipError_t he =
-          launch_rep(ps, [&] { return lr::run_colsum(W.colpart, tiles, d, gr->gamma2, st); });
-      if (he != hipSuccess) return hip_fail(he, "dgamma2");
+      cs_tiles = (T + bm - 1) / bm;
     }
-    // dA_gu = gamma2 * (dgus^T h)
+    // dA_gu = gamma2 * (dgus^T h); on the pipelined engine the
+    // kernel also sums the RMSNorm backward's per-tile column partials into
+    // dgamma2 (a side job after its own outputs), else a kernel of its own does.
     {
       lr::GemmDesc g;
       g.M = 2 * r;
@@ -1050,7 +1049,20 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.c[0] = gr->A_gu;
       g.ldc[0] = d;
       g.colscale = w->gamma2;
+      const bool side = lr::uses_engine2(lr::OP_TN_WGRAD, dt, g, 1);
+      if (side) {
+        g.cs_part = W.colpart;
+        g.cs_rows = cs_tiles;
+        g.cs_n = d;
+        g.cs_out = gr->gamma2;
+      }
       RUN(wgrad(dt, g, 1, W, st, "dA_gu", "dA_gu split-K sum"));
+      if (!side) {
+        ProfScope ps("dgamma2 column sum", st, 4.0 * cs_tiles * d + 4.0 * d, true);
+        hipError_t he = launch_rep(
+            ps, [&] { return lr::run_colsum(W.colpart, cs_tiles, d, gr->gamma2, st); });
+        if (he != hipSuccess) return hip_fail(he, "dgamma2");
+      }
     }
     // dB_o = dh^T o_r
     {
@@ -1177,13 +1189,11 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.colsum = W.colpart;
       RUN(gemm(lr::OP_NN_RMSBWD, dt, g, 1, st, "RMSNorm-1 backward"));
       const int bm = lr::gemm_tile_m_used(lr::OP_NN_RMSBWD, dt, g, 1);
-      const int tiles = (T + bm - 1) / bm;
-      ProfScope ps("dgamma1 column sum", st, 4.0 * tiles * d + 4.0 * d, true);
-      hipError_t he =
-          launch_rep(ps, [&] { return lr::run_colsum(W.colpart, tiles, d, gr->gamma1, st); });
-      if (he != hipSuccess) return hip_fail(he, "dgamma1");
+      cs_tiles = (T + bm - 1) / bm;
     }
-    // dA_qkv = gamma1 * (dqs^T X)
+    // dA_qkv = gamma1 * (dqs^T X); on the pipelined engine the
+    // kernel also sums the RMSNorm backward's per-tile column partials into
+    // dgamma1 (a side job after its own outputs), else a kernel of its own does.
     {
       lr::GemmDesc g;
       g.M = 3 * r;
@@ -1196,7 +1206,20 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.c[0] = gr->A_qkv;
       g.ldc[0] = d;
       g.colscale = w->gamma1;
+      const bool side = lr::uses_engine2(lr::OP_TN_WGRAD, dt, g, 1);
+      if (side) {
+        g.cs_part = W.colpart;
+        g.cs_rows = cs_tiles;
+        g.cs_n = d;
+        g.cs_out = gr->gamma1;
+      }
       RUN(wgrad(dt, g, 1, W, st, "dA_qkv", "dA_qkv split-K sum"));
+      if (!side) {
+        ProfScope ps("dgamma1 column sum", st, 4.0 * cs_tiles * d + 4.0 * d, true);
+        hipError_t he = launch_rep(
+            ps, [&] { return lr::run_colsum(W.colpart, cs_tiles, d, gr->gamma1, st); });
+        if (he != hipSuccess) return hip_fail(he, "dgamma1");
+      }
     }
   }
   return LR_OK;

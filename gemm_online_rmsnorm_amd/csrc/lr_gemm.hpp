@@ -70,6 +70,14 @@ struct GemmArgs {
   int groups;
   int ktiles_split;
   int64_t c_split_stride;
+  // Side job of the pipelined engine, run by every workgroup after its own
+  // outputs: cs_out[c] = sum over r = 0 .. cs_rows - 1 of
+  // cs_part[r * cs_n + c] in a fixed order (the gamma-gradient column sums
+  // of an RMSNorm backward launched before this kernel). Off when cs_out is
+  // null.
+  const float* cs_part;
+  int cs_rows, cs_n;
+  float* cs_out;
 };
 
 // ---------------------------------------------------------------------------

@@ -1321,6 +1321,23 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       if (n0 + c < N) g.colsum[(int64_t)tm * N + n0 + c] = sum;
     }
   }
+
+  // Side job: a share of the columns of an earlier kernel's per-tile column
+  // sums. A wave takes one column at a time: lane l adds rows l, l + 64, ...
+  // in order, then a fixed butterfly adds the 64 lanes (deterministic).
+  if (g.cs_out != nullptr) {
+    const int nwg = (int)(gridDim.x * gridDim.z);
+    const int wid = (int)(blockIdx.x + gridDim.x * blockIdx.z);
+    const int per = (g.cs_n + nwg - 1) / nwg;
+    const int cend = min(g.cs_n, (wid + 1) * per);
+    for (int c = wid * per + wave; c < cend; c += TL::NWAVE) {
+      float sum = 0.f;
+      for (int r = lane; r < g.cs_rows; r += 64) sum += g.cs_part[(int64_t)r * g.cs_n + c];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+      if (lane == 0) g.cs_out[c] = sum;
+    }
+  }
 #undef LR_E
 }
 

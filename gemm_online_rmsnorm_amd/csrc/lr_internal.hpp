@@ -46,6 +46,11 @@ struct GemmDesc {
   int emit_partial = 0;
   int ksplit = 1;                // split-K factor (pipelined engine only)
   int64_t c_split_stride = 0;    // output element stride between splits
+  // Column sums run as a side job after the outputs (pipelined engine only):
+  // cs_out[c] = sum_r cs_part[r * cs_n + c] in a fixed order.
+  const float* cs_part = nullptr;
+  int cs_rows = 0, cs_n = 0;
+  float* cs_out = nullptr;
 };
 
 // Tile sizes an operation uses for a dtype (0 = LR_F32, 1 = LR_BF16).

@@ -183,6 +183,10 @@ static hipError_t launch2(const GemmDesc& d, int groups, hipStream_t s) {
   const int split = d.ksplit > 1 ? d.ksplit : 1;
   g.ktiles_split = d.K / TL::BK / split;
   g.c_split_stride = d.c_split_stride;
+  g.cs_part = d.cs_part;
+  g.cs_rows = d.cs_rows;
+  g.cs_n = d.cs_n;
+  g.cs_out = d.cs_out;
   if (g.tiles_m == 0 || g.tiles_n == 0 || groups == 0) return hipSuccess;
   dim3 grid(g.tiles_m * g.tiles_n, 1, groups * split);
   hipLaunchKernelGGL(kern, grid, dim3(TL::NT), lds, s, g);
