@@ -215,6 +215,23 @@ struct BwdWs {
   size_t wpart_bytes;
 };
 
+// A weight-gradient (TN) descriptor: out [M, N] = a^T b over K rows.
+lr::GemmDesc tn_desc(int M, int N, int K, const void* a, int64_t lda, const void* b, int64_t ldb,
+                     float* c, const void* colscale) {
+  lr::GemmDesc g;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.a[0] = a;
+  g.lda[0] = lda;
+  g.b[0] = b;
+  g.ldb[0] = ldb;
+  g.c[0] = c;
+  g.ldc[0] = N;
+  g.colscale = colscale;
+  return g;
+}
+
 // Partial-sum workspace of the largest split-K weight gradient of the block:
 // (M, N, lda, ldb, groups) of every TN GEMM lr_block_bwd runs, K = T.
 size_t wgrad_part_max(const lr_block_shape* s) {
@@ -240,6 +257,21 @@ size_t wgrad_part_max(const lr_block_shape* s) {
       g.ldb[i] = sh[3];
     }
     const size_t b = lr::wgrad_part_bytes(s->dtype, g, (int)sh[4]);
+    mx = b > mx ? b : mx;
+  }
+  // The weight gradients that run together in one launch.
+  const int Ti = (int)T, di = (int)d, ri = (int)r;
+  const lr::GemmDesc g3[3] = {tn_desc(2 * ri, di, Ti, nullptr, 2 * r, nullptr, d, nullptr, nullptr),
+                              tn_desc(di, ri, Ti, nullptr, d, nullptr, r, nullptr, nullptr),
+                              tn_desc(ri, di, Ti, nullptr, r, nullptr, d, nullptr, nullptr)};
+  const lr::GemmDesc g2[2] = {tn_desc(3 * ri, di, Ti, nullptr, 3 * r, nullptr, d, nullptr, nullptr),
+                              tn_desc(di, ri, Ti, nullptr, d, nullptr, r, nullptr, nullptr)};
+  if (lr::wgrad_multi_ok(s->dtype, g3, 3)) {
+    const size_t b = lr::wgrad_multi_part_bytes(g3, 3, lr::wgrad_multi_split(g3, 3));
+    mx = b > mx ? b : mx;
+  }
+  if (lr::wgrad_multi_ok(s->dtype, g2, 2)) {
+    const size_t b = lr::wgrad_multi_part_bytes(g2, 2, lr::wgrad_multi_split(g2, 2));
     mx = b > mx ? b : mx;
   }
   return mx;
@@ -324,6 +356,31 @@ int wgrad(int dtype, const lr::GemmDesc& d, int groups, const BwdWs& W, hipStrea
           const char* what, const char* sum_name) {
   return wgrad(dtype, d, groups, W.wpart, W.wpart_bytes, st, what, sum_name);
 }
+
+// Weight gradients of n problems of different shapes in one launch (each
+// with its own output and column scale), K split over the workspace when
+// their tiles together are too few; then each problem's split-K sum.
+int wgrad_multi(int dtype, const lr::GemmDesc* p, int n, const BwdWs& W, hipStream_t st,
+                const char* what, const char* const* sum_names) {
+  const int splits = lr::wgrad_multi_split(p, n);
+  if (lr::wgrad_multi_part_bytes(p, n, splits) > W.wpart_bytes)
+    return fail(LR_ERR_WORKSPACE, "%s: split-K partials exceed the workspace", what);
+  {
+    ProfScope ps(what, st);
+    hipError_t e = lr::run_wgrad_multi_gemm(p, n, splits, W.wpart, st);
+    if (e != hipSuccess) return hip_fail(e, what);
+  }
+  for (int i = 0; splits > 1 && i < n; ++i) {
+    const float* part = static_cast<const float*>(W.wpart) + lr::wgrad_multi_part_offset(p, i, splits);
+    const double mn = (double)p[i].M * p[i].N;
+    ProfScope ps(sum_names[i], st, mn * 4.0 * (splits + 1) + (p[i].colscale ? 2.0 * p[i].N : 0.0),
+                 true);
+    hipError_t e = launch_rep(ps, [&] { return lr::run_wgrad_sum(p[i], 1, splits, part, st); });
+    if (e != hipSuccess) return hip_fail(e, sum_names[i]);
+  }
+  return LR_OK;
+}
+
 
 #define RUN(x)            \
   do {                    \
@@ -852,21 +909,15 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
   const float inv_D = 1.0f / (float)s->d_norm;
 
   int cs_tiles = 0;  // M-tiles of the RMSNorm backward (rows of its column partials)
+  // Weight gradients that run together, one launch per group, when their
+  // tiles fit the pipelined engine: dA_gu, dB_o, dA_o once do_r exists, and
+  // (whole backward in one call) dB_dn, held back to run beside dA_qkv.
+  const lr::GemmDesc dB_dn = tn_desc(d, r, T, dY, d, sv->d_r, r, gr->B_dn, nullptr);
+  lr::GemmDesc last2[2] = {tn_desc(3 * r, d, T, W.dqs, 3 * r, X, d, gr->A_qkv, w->gamma1), dB_dn};
+  const bool late_dbdn = stage == LR_STAGE_ALL && lr::wgrad_multi_ok(dt, last2, 2);
   if (post) {
     // dB_dn = dY^T d_r
-    {
-      lr::GemmDesc g;
-      g.M = d;
-      g.N = r;
-      g.K = T;
-      g.a[0] = dY;
-      g.lda[0] = d;
-      g.b[0] = sv->d_r;
-      g.ldb[0] = r;
-      g.c[0] = gr->B_dn;
-      g.ldc[0] = r;
-      RUN(wgrad(dt, g, 1, W, st, "dB_dn", "dB_dn split-K sum"));
-    }
+    if (!late_dbdn) RUN(wgrad(dt, dB_dn, 1, W, st, "dB_dn", "dB_dn split-K sum"));
     // dd_r = dY B_dn
     {
       lr::GemmDesc g;
@@ -1034,52 +1085,8 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       const int bm = lr::gemm_tile_m_used(lr::OP_NN_RMSBWD, dt, g, 1);
       cs_tiles = (T + bm - 1) / bm;
     }
-    // dA_gu = gamma2 * (dgus^T h); on the pipelined engine the
-    // kernel also sums the RMSNorm backward's per-tile column partials into
-    // dgamma2 (a side job after its own outputs), else a kernel of its own does.
-    {
-      lr::GemmDesc g;
-      g.M = 2 * r;
-      g.N = d;
-      g.K = T;
-      g.a[0] = W.dgus;
-      g.lda[0] = 2 * r;
-      g.b[0] = W.h;
-      g.ldb[0] = d;
-      g.c[0] = gr->A_gu;
-      g.ldc[0] = d;
-      g.colscale = w->gamma2;
-      const bool side = lr::uses_engine2(lr::OP_TN_WGRAD, dt, g, 1);
-      if (side) {
-        g.cs_part = W.colpart;
-        g.cs_rows = cs_tiles;
-        g.cs_n = d;
-        g.cs_out = gr->gamma2;
-      }
-      RUN(wgrad(dt, g, 1, W, st, "dA_gu", "dA_gu split-K sum"));
-      if (!side) {
-        ProfScope ps("dgamma2 column sum", st, 4.0 * cs_tiles * d + 4.0 * d, true);
-        hipError_t he = launch_rep(
-            ps, [&] { return lr::run_colsum(W.colpart, cs_tiles, d, gr->gamma2, st); });
-        if (he != hipSuccess) return hip_fail(he, "dgamma2");
-      }
-    }
-    // dB_o = dh^T o_r
-    {
-      lr::GemmDesc g;
-      g.M = d;
-      g.N = r;
-      g.K = T;
-      g.a[0] = W.dh;
-      g.lda[0] = d;
-      g.b[0] = sv->o_r;
-      g.ldb[0] = r;
-      g.c[0] = gr->B_o;
-      g.ldc[0] = r;
-      RUN(wgrad(dt, g, 1, W, st, "dB_o", "dB_o split-K sum"));
-    }
     // do_r = dh B_o
-    {
+    auto do_r_gemm = [&]() {
       lr::GemmDesc g;
       g.M = T;
       g.N = r;
@@ -1090,21 +1097,38 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.ldb[0] = r;
       g.c[0] = W.do_r;
       g.ldc[0] = r;
-      RUN(gemm(lr::OP_NN_STORE, dt, g, 1, st, "do_r"));
+      return gemm(lr::OP_NN_STORE, dt, g, 1, st, "do_r");
+    };
+    // dA_gu = gamma2 * (dgus^T h), dB_o = dh^T o_r, dA_o = do_r^T O. On the
+    // pipelined engine the (first) launch also sums the RMSNorm backward's
+    // per-tile column partials into dgamma2 as a side job after its own
+    // outputs; otherwise a kernel of its own does.
+    lr::GemmDesc mid3[3] = {tn_desc(2 * r, d, T, W.dgus, 2 * r, W.h, d, gr->A_gu, w->gamma2),
+                            tn_desc(d, r, T, W.dh, d, sv->o_r, r, gr->B_o, nullptr),
+                            tn_desc(r, d, T, W.do_r, r, O_attn, d, gr->A_o, nullptr)};
+    const bool side2 = lr::uses_engine2(lr::OP_TN_WGRAD, dt, mid3[0], 1);
+    if (side2) {
+      mid3[0].cs_part = W.colpart;
+      mid3[0].cs_rows = cs_tiles;
+      mid3[0].cs_n = d;
+      mid3[0].cs_out = gr->gamma2;
     }
-    // dA_o = do_r^T O
-    {
-      lr::GemmDesc g;
-      g.M = r;
-      g.N = d;
-      g.K = T;
-      g.a[0] = W.do_r;
-      g.lda[0] = r;
-      g.b[0] = O_attn;
-      g.ldb[0] = d;
-      g.c[0] = gr->A_o;
-      g.ldc[0] = d;
-      RUN(wgrad(dt, g, 1, W, st, "dA_o", "dA_o split-K sum"));
+    if (lr::wgrad_multi_ok(dt, mid3, 3)) {
+      RUN(do_r_gemm());
+      static const char* const sums[3] = {"dA_gu split-K sum", "dB_o split-K sum",
+                                          "dA_o split-K sum"};
+      RUN(wgrad_multi(dt, mid3, 3, W, st, "dA_gu, dB_o, dA_o", sums));
+    } else {
+      RUN(wgrad(dt, mid3[0], 1, W, st, "dA_gu", "dA_gu split-K sum"));
+      RUN(wgrad(dt, mid3[1], 1, W, st, "dB_o", "dB_o split-K sum"));
+      RUN(do_r_gemm());
+      RUN(wgrad(dt, mid3[2], 1, W, st, "dA_o", "dA_o split-K sum"));
+    }
+    if (!side2) {
+      ProfScope ps("dgamma2 column sum", st, 4.0 * cs_tiles * d + 4.0 * d, true);
+      hipError_t he = launch_rep(
+          ps, [&] { return lr::run_colsum(W.colpart, cs_tiles, d, gr->gamma2, st); });
+      if (he != hipSuccess) return hip_fail(he, "dgamma2");
     }
     // dO = do_r A_o
     {
@@ -1191,35 +1215,27 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       const int bm = lr::gemm_tile_m_used(lr::OP_NN_RMSBWD, dt, g, 1);
       cs_tiles = (T + bm - 1) / bm;
     }
-    // dA_qkv = gamma1 * (dqs^T X); on the pipelined engine the
-    // kernel also sums the RMSNorm backward's per-tile column partials into
-    // dgamma1 (a side job after its own outputs), else a kernel of its own does.
-    {
-      lr::GemmDesc g;
-      g.M = 3 * r;
-      g.N = d;
-      g.K = T;
-      g.a[0] = W.dqs;
-      g.lda[0] = 3 * r;
-      g.b[0] = X;
-      g.ldb[0] = d;
-      g.c[0] = gr->A_qkv;
-      g.ldc[0] = d;
-      g.colscale = w->gamma1;
-      const bool side = lr::uses_engine2(lr::OP_TN_WGRAD, dt, g, 1);
-      if (side) {
-        g.cs_part = W.colpart;
-        g.cs_rows = cs_tiles;
-        g.cs_n = d;
-        g.cs_out = gr->gamma1;
-      }
-      RUN(wgrad(dt, g, 1, W, st, "dA_qkv", "dA_qkv split-K sum"));
-      if (!side) {
-        ProfScope ps("dgamma1 column sum", st, 4.0 * cs_tiles * d + 4.0 * d, true);
-        hipError_t he = launch_rep(
-            ps, [&] { return lr::run_colsum(W.colpart, cs_tiles, d, gr->gamma1, st); });
-        if (he != hipSuccess) return hip_fail(he, "dgamma1");
-      }
+    // dA_qkv = gamma1 * (dqs^T X) (with dB_dn beside it when held back); on
+    // the pipelined engine the launch also sums the RMSNorm backward's
+    // per-tile column partials into dgamma1, else a kernel of its own does.
+    const bool side1 = lr::uses_engine2(lr::OP_TN_WGRAD, dt, last2[0], 1);
+    if (side1) {
+      last2[0].cs_part = W.colpart;
+      last2[0].cs_rows = cs_tiles;
+      last2[0].cs_n = d;
+      last2[0].cs_out = gr->gamma1;
+    }
+    if (late_dbdn) {
+      static const char* const sums[2] = {"dA_qkv split-K sum", "dB_dn split-K sum"};
+      RUN(wgrad_multi(dt, last2, 2, W, st, "dA_qkv, dB_dn", sums));
+    } else {
+      RUN(wgrad(dt, last2[0], 1, W, st, "dA_qkv", "dA_qkv split-K sum"));
+    }
+    if (!side1) {
+      ProfScope ps("dgamma1 column sum", st, 4.0 * cs_tiles * d + 4.0 * d, true);
+      hipError_t he = launch_rep(
+          ps, [&] { return lr::run_colsum(W.colpart, cs_tiles, d, gr->gamma1, st); });
+      if (he != hipSuccess) return hip_fail(he, "dgamma1");
     }
   }
   return LR_OK;

@@ -78,6 +78,16 @@ struct GemmArgs {
   const float* cs_part;
   int cs_rows, cs_n;
   float* cs_out;
+  // Up to three problems of different M, N (same K) in one launch (weight
+  // gradients, pipelined engine), when nprob > 0: after the XCD remapping
+  // the workgroups [prob_base[p], prob_base[p + 1]) run problem p's
+  // tiles_mp[p] x tiles_np[p] tiles, and slot p of the operand arrays is
+  // problem p's, with its own M, N, column scale and element stride
+  // between split-K slices. blockIdx.z is then the split.
+  int nprob;
+  int Mp[3], Np[3], tiles_mp[3], tiles_np[3], prob_base[4];
+  const void* colscales[3];
+  int64_t csplit[3];
 };
 
 // ---------------------------------------------------------------------------
@@ -227,14 +237,15 @@ __device__ __forceinline__ void mfma_step<float>(const u32x4& a, const u32x4& b,
 // hardware deals workgroups to the 8 XCDs round-robin) get consecutive
 // logical ids, which walk GROUP_M M-tiles before the next N-tile so that the
 // XCD's L2 serves both operands' tiles to several workgroups.
-template <int GROUP_M = 8>
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+__device__ __forceinline__ int xcd_logical(int nwg) {
   constexpr int NXCD = 8;
-  const int nwg = tiles_m * tiles_n;
   const int pid = blockIdx.x;
   const int q = nwg / NXCD, rem = nwg % NXCD;
   const int x = pid % NXCD;
-  const int logical = x * q + (x < rem ? x : rem) + pid / NXCD;
+  return x * q + (x < rem ? x : rem) + pid / NXCD;
+}
+template <int GROUP_M = 8>
+__device__ __forceinline__ void group_tile(int logical, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int in_group = GROUP_M * tiles_n;
   const int gid = logical / in_group;
   const int first_m = gid * GROUP_M;
@@ -242,6 +253,10 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   const int l = logical % in_group;
   tm = first_m + l % gsize;
   tn = l / gsize;
+}
+template <int GROUP_M = 8>
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  group_tile<GROUP_M>(xcd_logical(tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
 // LDS bytes used by the main loop.

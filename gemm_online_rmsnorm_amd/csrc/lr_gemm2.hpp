@@ -547,11 +547,28 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   // tile, whose rows carry two A operands, that is 7.3 MB of operands at the
   // 7B shape against 8.4 MB for 8 x 4 (measured: 6% faster SwiGLU tiles,
   // 2-6% faster one-pair tiles, 5% fewer L2 misses).
-  tile_coords<4>(g.tiles_m, g.tiles_n, tm, tn);
+  // With several problems in one launch (nprob > 0) the workgroup's problem
+  // is its slot: shape, column scale and split stride come from its entry.
+  int slot, M, N;
+  const void* colscale = g.colscale;
+  int64_t csplit = g.c_split_stride;
+  if (NPAIR == 1 && g.nprob > 0) {
+    const int lg = xcd_logical((int)gridDim.x);
+    slot = wave_uniform(lg >= g.prob_base[2] ? 2 : (lg >= g.prob_base[1] ? 1 : 0));
+    M = pick3(g.Mp, slot);
+    N = pick3(g.Np, slot);
+    const int base = slot == 0 ? 0 : (slot == 1 ? g.prob_base[1] : g.prob_base[2]);
+    group_tile<4>(lg - base, pick3(g.tiles_mp, slot), pick3(g.tiles_np, slot), tm, tn);
+    colscale = pick3(g.colscales, slot);
+    csplit = pick3(g.csplit, slot);
+  } else {
+    tile_coords<4>(g.tiles_m, g.tiles_n, tm, tn);
+    slot = (NPAIR == 1) ? (int)blockIdx.z % g.groups : 0;
+    M = g.M;
+    N = g.N;
+  }
   const int m0 = tm * BM, n0 = tn * BNO;
-  const int slot = (NPAIR == 1) ? (int)blockIdx.z % g.groups : 0;
   const int split = (int)blockIdx.z / g.groups;
-  const int M = g.M, N = g.N;
 
   // With two waves per SIMD the SIMD serves the older wave's MFMAs first,
   // so the younger one (waves NWAVE / 2 ..) ends each K-tile alone while
@@ -971,10 +988,10 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   if constexpr (HAS_GAMMA) {
 #if defined(__HIP_DEVICE_COMPILE__)
     // Columns past the end read as zero; no gamma array means gamma = 1.
-    const bool gon = g.colscale != nullptr;
+    const bool gon = colscale != nullptr;
     const unsigned char* gp;
     int gbytes;
-    epi_range(g.colscale, 2, 0, 0, n0, 1, N, gp, gbytes);
+    epi_range(colscale, 2, 0, 0, n0, 1, N, gp, gbytes);
     const __amdgpu_buffer_rsrc_t grs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(gp), (short)0, gbytes, 0x00020000);
 #pragma unroll
@@ -1301,7 +1318,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
           const f32x4 x = LR_E(0, i, j);
           __builtin_nontemporal_store(
               f32x4{x[0] * gmv[j][0], x[1] * gmv[j][1], x[2] * gmv[j][2], x[3] * gmv[j][3]},
-              reinterpret_cast<f32x4*>(static_cast<float*>(pick3(g.c, slot)) + split * g.c_split_stride +
+              reinterpret_cast<f32x4*>(static_cast<float*>(pick3(g.c, slot)) + split * csplit +
                                        (int64_t)gr * pick3(g.ldc, slot) + gc));
         }
       }

@@ -83,6 +83,19 @@ hipError_t run_wgrad_gemm(int dtype, const GemmDesc& d, int groups, int splits, 
 hipError_t run_wgrad_sum(const GemmDesc& d, int groups, int splits, const void* part,
                          hipStream_t s);
 
+// Weight gradients of up to three problems of different M, N (same K) in one
+// launch, problem i writing p[i].c[0] (column scale p[i].colscale); the
+// column-sum side job is taken from p[0]. wgrad_multi_ok: all of them can
+// run so; wgrad_multi_split: the K-split for their tiles together (1: none);
+// with a split the partials of problem i lie at part +
+// wgrad_multi_part_offset(p, i, splits) floats, and run_wgrad_sum then
+// adds each problem's slices (as a one-group call on those partials).
+bool wgrad_multi_ok(int dtype, const GemmDesc* p, int n);
+int wgrad_multi_split(const GemmDesc* p, int n);
+size_t wgrad_multi_part_bytes(const GemmDesc* p, int n, int splits);
+int64_t wgrad_multi_part_offset(const GemmDesc* p, int i, int splits);
+hipError_t run_wgrad_multi_gemm(const GemmDesc* p, int n, int splits, void* part, hipStream_t s);
+
 // Memory-bound helpers.
 hipError_t run_fold_gamma(int dtype, const void* A, int64_t lda, const void* gamma, void* out,
                           int rows, int cols, hipStream_t s);

@@ -425,6 +425,112 @@ hipError_t run_wgrad_sum(const GemmDesc& d, int groups, int splits, const void* 
   return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// Weight gradients of up to three problems with different M, N (same K) in
+// one launch: problems whose 256 x 256 grids are each too small for the GPU
+// but together fill it run whole-K tiles side by side instead of splitting
+// K (no partial sums); with fewer tiles than that K is still split, the
+// partials of problem i at part + off_i (slices M_i N_i apart).
+// ---------------------------------------------------------------------------
+bool wgrad_multi_ok(int dtype, const GemmDesc* p, int n) {
+  if (dtype != 1 || n < 1 || n > 3) return false;
+  for (int i = 0; i < n; ++i) {
+    if (p[i].K != p[0].K || p[i].N % 4 != 0 || !wgrad_big_tile(p[i])) return false;
+    if (!uses_engine2(OP_TN_WGRAD, dtype, p[i], 1)) return false;
+  }
+  return true;
+}
+
+int wgrad_multi_split(const GemmDesc* p, int n) {
+  int64_t t = 0;
+  for (int i = 0; i < n; ++i) t += ntiles(p[i], 256, 256, 1);
+  const int nk = p[0].K / 64;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int sp : {1, 2, 3, 4, 6, 8}) {
+    if (nk % sp != 0 || nk / sp < 4) continue;
+    const double waves = (double)((t * sp + kCUs - 1) / kCUs);
+    const double cost = waves / sp + 0.03 * (sp - 1);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = sp;
+    }
+  }
+  return best;
+}
+
+size_t wgrad_multi_part_bytes(const GemmDesc* p, int n, int splits) {
+  if (splits <= 1) return 0;
+  size_t b = 0;
+  for (int i = 0; i < n; ++i) b += (size_t)splits * (size_t)p[i].M * p[i].N * sizeof(float);
+  return b;
+}
+
+int64_t wgrad_multi_part_offset(const GemmDesc* p, int i, int splits) {
+  int64_t off = 0;
+  for (int j = 0; j < i; ++j) off += (int64_t)splits * p[j].M * p[j].N;
+  return off;
+}
+
+template <class TL>
+static hipError_t launch2_multi(const GemmDesc* p, int n, int splits, float* part, hipStream_t s) {
+  auto kern = gemm2_kernel<TL, 1, 3u, EPI_WGRAD>;
+  constexpr int lds = gemm2_lds_bytes<TL, 1, EPI_WGRAD>();
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [&] {
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  GemmArgs g{};
+  g.K = p[0].K;
+  g.groups = 1;
+  g.ktiles_split = p[0].K / TL::BK / splits;
+  g.nprob = n;
+  int base = 0;
+  for (int i = 0; i < 3; ++i) {
+    const GemmDesc& d = p[i < n ? i : n - 1];
+    const bool live = i < n;
+    g.a[i] = d.a[0];
+    g.lda[i] = d.lda[0];
+    g.b[i] = d.b[0];
+    g.ldb[i] = d.ldb[0];
+    g.Mp[i] = d.M;
+    g.Np[i] = d.N;
+    g.tiles_mp[i] = (d.M + TL::BM - 1) / TL::BM;
+    g.tiles_np[i] = (d.N + TL::BNO - 1) / TL::BNO;
+    g.prob_base[i] = base;
+    if (live) base += g.tiles_mp[i] * g.tiles_np[i];
+    if (splits > 1) {
+      g.c[i] = part + wgrad_multi_part_offset(p, i < n ? i : n - 1, splits);
+      g.ldc[i] = d.N;
+      g.colscales[i] = nullptr;
+    } else {
+      g.c[i] = d.c[0];
+      g.ldc[i] = d.ldc[0];
+      g.colscales[i] = d.colscale;
+    }
+    g.csplit[i] = (int64_t)d.M * d.N;
+  }
+  // Problems past n start past the last workgroup.
+  for (int i = n; i < 3; ++i) g.prob_base[i] = base;
+  g.prob_base[3] = base;
+  g.cs_part = p[0].cs_part;
+  g.cs_rows = p[0].cs_rows;
+  g.cs_n = p[0].cs_n;
+  g.cs_out = p[0].cs_out;
+  if (base == 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(base, 1, splits), dim3(TL::NT), lds, s, g);
+  return hipGetLastError();
+}
+
+hipError_t run_wgrad_multi_gemm(const GemmDesc* p, int n, int splits, void* part, hipStream_t s) {
+  float* pf = static_cast<float*>(part);
+  if (splits <= 2) return launch2_multi<P256x256a>(p, n, splits, pf, s);
+  return launch2_multi<P256x256>(p, n, splits, pf, s);
+}
+
 hipError_t run_gemm(int op, int dtype, const GemmDesc& d, int groups, hipStream_t s) {
   if (uses_engine2(op, dtype, d, groups)) return run_gemm2(op, d, groups, s);
   if (op == OP_SWIGLU_BWD2) return hipErrorInvalidValue;  // pipelined engine only

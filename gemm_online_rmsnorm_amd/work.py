@@ -65,6 +65,10 @@ def kernel_work(T: int, d: int, r: int, F: int, elem: int = 2, partials: bool = 
     g("RMSNorm-1 backward", T, d, 3 * r, extra_in=2 * e * T * d + 4 * T + e * d)
     W["dgamma1 column sum"] = (0.0, 4 * ((T + 255) // 256) * d + 4 * d)
     g("dA_qkv", 3 * r, d, T, out_elem=4, extra_in=e * d)
+    # weight gradients that run together in one launch
+    for name, parts in (("dA_gu, dB_o, dA_o", ("dA_gu", "dB_o", "dA_o")),
+                        ("dA_qkv, dB_dn", ("dA_qkv", "dB_dn"))):
+        W[name] = (sum(W[k][0] for k in parts), sum(W[k][1] for k in parts))
     return W
 
 

@@ -29,6 +29,13 @@ CASES = {
     # two k-tiles and of one
     "bf16-gateup-r128": S("bf16-gateup-r128", T=4100, d=512, r=128, F=2112, D=512, seed=26),
     "bf16-gateup-r64": S("bf16-gateup-r64", T=4100, d=256, r=64, F=2104, D=256, seed=27),
+    # weight gradients of several shapes in one launch (dA_gu, dB_o, dA_o;
+    # dA_qkv with dB_dn): with K split over per-problem partials (16 k-tiles)
+    # and unsplit with ragged tiles (17 k-tiles, d and r not multiples of 256)
+    "bf16-wgrad-group-split": S("bf16-wgrad-group-split", T=1024, d=1024, r=256, F=704,
+                                D=1024, seed=28),
+    "bf16-wgrad-group-ragged": S("bf16-wgrad-group-ragged", T=1088, d=1280, r=320, F=832,
+                                 D=1280, seed=29),
 }
 
 
