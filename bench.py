@@ -68,6 +68,11 @@ def _parse():
                     help="instead of the block step: time torch.matmul (hipBLASLt) on plain "
                          "GEMMs of the config's shapes, a reference point for the library's "
                          "fused kernels (no fusion, random operands)")
+    ap.add_argument("--gemm-sweep", action="store_true",
+                    help="instead of the block step: time one-pair products of the block's "
+                         "widths (16384 x 4096, NT, NT with a residual, NN; 4096 x 4096 TN) at "
+                         "K = 1024 ... 8192 through the C ABI and fit time = a + b K, the "
+                         "per-launch fixed cost and the main-loop rate")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"first make one device copy of {COPY_BYTES} bytes, the reference "
                          "rocprofv3 byte counters are scaled by")
@@ -253,6 +258,86 @@ def vendor_gemms_main(args, s):
                                 "shapes (reference point)", "n_gpus": 1,
                       "config": {"workload": s.name, "tokens": T, "d": d, "r": r, "d_ff": F},
                       "gemms": out}), flush=True)
+
+
+def gemm_sweep_main(args):
+    """One JSON line: per-launch time of single products through
+    lr_grouped_lowrank_gemm at K = 1024, 2048, 4096, 8192 (M = 16384,
+    N = 4096; the weight gradient 4096 x 4096 over K), and the least-squares
+    fit time = a + b * K per product: a is the per-launch cost that does not
+    grow with K (prologue, epilogue, launch), b the main loop's time per k."""
+    import ctypes
+    import torch
+    from gemm_online_rmsnorm_amd import _lib
+
+    lib = _lib.load()
+    P = _lib.lr_gemm_pair
+    g = torch.Generator(device="cuda").manual_seed(0)
+    M, N, KMAX = 16384, 4096, 8192
+
+    def rnd(*shape, scale=1.0):
+        return (torch.randn(*shape, device="cuda", generator=g) * scale).to(torch.bfloat16)
+
+    X, Wt, Wn = rnd(M, KMAX), rnd(N, KMAX, scale=0.01), rnd(KMAX, N, scale=0.01)
+    Y, R = torch.empty(M, N, device="cuda", dtype=torch.bfloat16), rnd(M, N)
+    A, B = rnd(KMAX, N), rnd(KMAX, N)
+    C = torch.empty(N, N, device="cuda", dtype=torch.float32)
+    ws = torch.empty(64 << 20, device="cuda", dtype=torch.uint8)
+    st = torch.cuda.current_stream().cuda_stream
+    x, wt, wn, y, r = X.data_ptr(), Wt.data_ptr(), Wn.data_ptr(), Y.data_ptr(), R.data_ptr()
+    ks = (1024, 2048, 4096, 8192)
+    prods = {
+        "NT": lambda K: (P(M, N, K, x, KMAX, wt, KMAX, y, N, None, 0), 0, 0, 2.0 * M * N * K),
+        "NT + residual": lambda K: (P(M, N, K, x, KMAX, wt, KMAX, y, N, r, N), 0, 1,
+                                    2.0 * M * N * K),
+        "NN": lambda K: (P(M, N, K, x, KMAX, wn, N, y, N, None, 0), 1, 0, 2.0 * M * N * K),
+        "TN (weight gradient)": lambda K: (P(N, N, K, A.data_ptr(), N, B.data_ptr(), N,
+                                             C.data_ptr(), N, None, 0), 2, 0, 2.0 * N * N * K),
+    }
+    # Every (product, K) point once per round, in turn, over three rounds; a
+    # point keeps its fastest round (the clock moves with the power draw).
+    best = {}
+    for _ in range(3):
+        for name, mk in prods.items():
+            for K in ks:
+                pair, layout, epi, flop = mk(K)
+                arr = (P * 1)(pair)
+                nbytes = int(lib.lr_grouped_lowrank_gemm_workspace_bytes(1, arr, _lib.LR_BF16,
+                                                                         layout))
+                assert nbytes <= ws.numel()
+
+                def call():
+                    _lib.check(lib.lr_grouped_lowrank_gemm_ws(
+                        1, arr, _lib.LR_BF16, layout, epi, ctypes.c_void_p(ws.data_ptr()),
+                        ws.numel(), st))
+                for _ in range(max(1, args.warmup)):
+                    call()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(args.steps):
+                    call()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / args.steps * 1e3
+                best[name, K] = min(best.get((name, K), us), us)
+    out = []
+    for name, mk in prods.items():
+        pts = [{"K": K, "us": round(best[name, K], 1),
+                "tflops": round(mk(K)[3] / best[name, K] / 1e6, 1)} for K in ks]
+        n = len(ks)
+        mk_, mt = sum(ks) / n, sum(p["us"] for p in pts) / n
+        b = (sum((k - mk_) * (p["us"] - mt) for k, p in zip(ks, pts))
+             / sum((k - mk_) ** 2 for k in ks))
+        a = mt - b * mk_
+        flop_per_k = mk(1)[3]
+        out.append({"product": name, "points": pts, "fixed_us": round(a, 1),
+                    "us_per_1024_k": round(b * 1024, 2),
+                    "main_loop_tflops": round(flop_per_k / (b * 1e-6) / 1e12, 1)})
+    print(json.dumps({"metric": "one-pair product time vs K (C ABI, bf16)", "n_gpus": 1,
+                      "steps": args.steps, "config": {"M": M, "N": N, "tn_out": [N, N]},
+                      "products": out}), flush=True)
 
 
 def _blas_threads():
@@ -487,6 +572,9 @@ def main():
         return
     if args.tp_split:
         tp_split_main(args, s)
+        return
+    if args.gemm_sweep:
+        gemm_sweep_main(args)
         return
     print(f"[bench] workload {s.name} T={s.T} d={s.d} r={s.r} F={s.F} D={s.D} P={s.P}",
           file=sys.stderr, flush=True)

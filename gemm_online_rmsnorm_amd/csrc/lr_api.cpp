@@ -698,10 +698,20 @@ int lr_block_fwd(const lr_block_shape* s, const lr_block_weights* w, const void*
   float* ssp1 = (!part && pt && s->n_panels > 1) ? pt->ss1 : nullptr;
   float* ssp2 = (!part && pt && s->n_panels > 1) ? pt->ss2 : nullptr;
 
+  // gamma1 and gamma2 folded into copies of the grouped down-projection
+  // weights (one launch when both stages run).
+  if (pre && post) {
+    ProfScope ps("fold gamma1, gamma2", st, (double)e * (2.0 * 5 * r * d + 2 * d), true);
+    hipError_t he = launch_rep(ps, [&] {
+      return lr::run_fold_gamma2(dt, w->A_qkv, d, w->gamma1, W.Ag_qkv, 3 * r, w->A_gu, d,
+                                 w->gamma2, W.Ag_gu, 2 * r, d, st);
+    });
+    if (he != hipSuccess) return hip_fail(he, "fold gamma");
+  }
   if (pre) {
     // Online RMSNorm + grouped [A_q; A_k; A_v] down-projection.
-    hipError_t he;
-    {
+    hipError_t he = hipSuccess;
+    if (!post) {
       ProfScope ps("fold gamma1", st, (double)e * (2.0 * 3 * r * d + d), true);
       he = launch_rep(ps, [&] {
         return lr::run_fold_gamma(dt, w->A_qkv, d, w->gamma1, W.Ag_qkv, 3 * r, d, st);
@@ -780,8 +790,8 @@ int lr_block_fwd(const lr_block_shape* s, const lr_block_weights* w, const void*
     hgm.ldres = d;
     RUN(gemm(lr::OP_NT_STORE, dt, hgm, 1, st, "O up-projection + residual"));
     // Online RMSNorm + grouped [A_g; A_u] down-projection.
-    hipError_t he;
-    {
+    hipError_t he = hipSuccess;
+    if (!pre) {
       ProfScope ps("fold gamma2", st, (double)e * (2.0 * 2 * r * d + d), true);
       he = launch_rep(ps, [&] {
         return lr::run_fold_gamma(dt, w->A_gu, d, w->gamma2, W.Ag_gu, 2 * r, d, st);

@@ -99,6 +99,10 @@ hipError_t run_wgrad_multi_gemm(const GemmDesc* p, int n, int splits, void* part
 // Memory-bound helpers.
 hipError_t run_fold_gamma(int dtype, const void* A, int64_t lda, const void* gamma, void* out,
                           int rows, int cols, hipStream_t s);
+// Two folds of the same width in one launch (job 0's rows, then job 1's).
+hipError_t run_fold_gamma2(int dtype, const void* A0, int64_t lda0, const void* g0, void* o0,
+                           int rows0, const void* A1, int64_t lda1, const void* g1, void* o1,
+                           int rows1, int cols, hipStream_t s);
 hipError_t run_rowdot_coef(int dtype, const void* a, int64_t lda, const void* b, int64_t ldb,
                            int width, const float* rms, float inv_D, float* coef, int rows,
                            hipStream_t s);

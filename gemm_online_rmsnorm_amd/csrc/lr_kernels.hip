@@ -542,21 +542,34 @@ hipError_t run_gemm(int op, int dtype, const GemmDesc& d, int groups, hipStream_
 // Memory-bound kernels
 // ---------------------------------------------------------------------------
 
-// out[n, k] = A[n, k] * gamma[k] (rounded to the storage type).
+// out[n, k] = A[n, k] * gamma[k] (rounded to the storage type), for one or
+// two (A, gamma, out) jobs of the same width in one launch: rows [0, rows0)
+// are job 0's, the next rows1 job 1's.
 template <typename T>
-__global__ __launch_bounds__(256) void fold_gamma_kernel(const T* __restrict__ A, int64_t lda,
-                                                         const T* __restrict__ gamma,
-                                                         T* __restrict__ out, int rows,
-                                                         int cols) {
+struct FoldJob {
+  const T* A;
+  int64_t lda;
+  const T* gamma;
+  T* out;
+  int rows;
+};
+template <typename T>
+__global__ __launch_bounds__(256) void fold_gamma_kernel(FoldJob<T> j0, FoldJob<T> j1, int cols) {
   constexpr int VEC = Elem<T>::VEC;
   const int vpr = cols / VEC;
-  const int64_t total = (int64_t)rows * vpr;
+  const int64_t total0 = (int64_t)j0.rows * vpr, total = total0 + (int64_t)j1.rows * vpr;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int r = (int)(i / vpr), c = (int)(i % vpr) * VEC;
+    const bool first = i < total0;
+    const int64_t li = first ? i : i - total0;
+    const int r = (int)(li / vpr), c = (int)(li % vpr) * VEC;
+    const T* A = first ? j0.A : j1.A;
+    const T* gmp = first ? j0.gamma : j1.gamma;
+    T* out = first ? j0.out : j1.out;
+    const int64_t lda = first ? j0.lda : j1.lda;
     float a[VEC], gm[VEC];
     unpack16<T>(*reinterpret_cast<const u32x4*>(A + r * lda + c), a);
-    unpack16<T>(*reinterpret_cast<const u32x4*>(gamma + c), gm);
+    unpack16<T>(*reinterpret_cast<const u32x4*>(gmp + c), gm);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) a[e] *= gm[e];
     *reinterpret_cast<u32x4*>(out + (int64_t)r * cols + c) = pack16<T>(a);
@@ -654,19 +667,34 @@ static int grid_for(int64_t work, int per_block) {
   return (int)g;
 }
 
+template <typename T>
+static hipError_t fold2(const void* A0, int64_t lda0, const void* g0, void* o0, int rows0,
+                        const void* A1, int64_t lda1, const void* g1, void* o1, int rows1,
+                        int cols, hipStream_t s) {
+  const FoldJob<T> j0{static_cast<const T*>(A0), lda0, static_cast<const T*>(g0),
+                      static_cast<T*>(o0), rows0};
+  const FoldJob<T> j1{static_cast<const T*>(A1 ? A1 : A0), A1 ? lda1 : lda0,
+                      static_cast<const T*>(A1 ? g1 : g0), static_cast<T*>(A1 ? o1 : o0),
+                      A1 ? rows1 : 0};
+  const int64_t chunks = ((int64_t)j0.rows + j1.rows) * cols / Elem<T>::VEC;
+  hipLaunchKernelGGL(fold_gamma_kernel<T>, dim3(grid_for(chunks, 256)), dim3(256), 0, s, j0, j1,
+                     cols);
+  return hipGetLastError();
+}
+
 hipError_t run_fold_gamma(int dtype, const void* A, int64_t lda, const void* gamma, void* out,
                           int rows, int cols, hipStream_t s) {
-  if (dtype == 0) {
-    hipLaunchKernelGGL(fold_gamma_kernel<float>, dim3(grid_for((int64_t)rows * cols / 4, 256)),
-                       dim3(256), 0, s, static_cast<const float*>(A), lda,
-                       static_cast<const float*>(gamma), static_cast<float*>(out), rows, cols);
-  } else {
-    hipLaunchKernelGGL(fold_gamma_kernel<bf16_t>, dim3(grid_for((int64_t)rows * cols / 8, 256)),
-                       dim3(256), 0, s, static_cast<const bf16_t*>(A), lda,
-                       static_cast<const bf16_t*>(gamma), static_cast<bf16_t*>(out), rows,
-                       cols);
-  }
-  return hipGetLastError();
+  return dtype == 0 ? fold2<float>(A, lda, gamma, out, rows, nullptr, 0, nullptr, nullptr, 0,
+                                   cols, s)
+                    : fold2<bf16_t>(A, lda, gamma, out, rows, nullptr, 0, nullptr, nullptr, 0,
+                                    cols, s);
+}
+
+hipError_t run_fold_gamma2(int dtype, const void* A0, int64_t lda0, const void* g0, void* o0,
+                           int rows0, const void* A1, int64_t lda1, const void* g1, void* o1,
+                           int rows1, int cols, hipStream_t s) {
+  return dtype == 0 ? fold2<float>(A0, lda0, g0, o0, rows0, A1, lda1, g1, o1, rows1, cols, s)
+                    : fold2<bf16_t>(A0, lda0, g0, o0, rows0, A1, lda1, g1, o1, rows1, cols, s);
 }
 
 hipError_t run_rowdot_coef(int dtype, const void* a, int64_t lda, const void* b, int64_t ldb,

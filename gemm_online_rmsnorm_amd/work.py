@@ -28,6 +28,7 @@ def kernel_work(T: int, d: int, r: int, F: int, elem: int = 2, partials: bool = 
     g("O down-projection", T, r, d)
     g("O up-projection + residual", T, d, r, extra_in=e * T * d)
     W["fold gamma2"] = (0.0, e * (2 * 2 * r * d + d))
+    W["fold gamma1, gamma2"] = (0.0, e * (2 * 5 * r * d + 2 * d))
     g("gate/up Online RMSNorm GEMM", T, 2 * r, d, extra_in=4 * T * (n_panels + 1))
     if partials:
         W["gate/up finalize"] = (0.0, e * 2 * T * 2 * r + 8 * T)
@@ -75,7 +76,8 @@ def kernel_work(T: int, d: int, r: int, F: int, elem: int = 2, partials: bool = 
 # Kernels bounded by HBM bandwidth rather than by the matrix cores (the
 # fixed-order sums of split-K weight-gradient slices are named
 # "<weight gradient> split-K sum").
-MEMORY_BOUND = ("fold gamma1", "fold gamma2", "QKV finalize", "gate/up finalize",
+MEMORY_BOUND = ("fold gamma1", "fold gamma2", "fold gamma1, gamma2", "fold gamma",
+                "QKV finalize", "gate/up finalize",
                 "row dot 1", "row dot 2", "dgamma1 column sum", "dgamma2 column sum")
 
 
