@@ -88,6 +88,10 @@ struct GemmArgs {
   int Mp[3], Np[3], tiles_mp[3], tiles_np[3], prob_base[4];
   const void* colscales[3];
   int64_t csplit[3];
+  // Persistent launches (pipelined engine, kernels that walk their tiles):
+  // tiles_m x tiles_n x groups tiles, workgroup b running tiles b,
+  // b + gridDim.x, ...
+  int vtiles;
 };
 
 // ---------------------------------------------------------------------------
@@ -237,13 +241,13 @@ __device__ __forceinline__ void mfma_step<float>(const u32x4& a, const u32x4& b,
 // hardware deals workgroups to the 8 XCDs round-robin) get consecutive
 // logical ids, which walk GROUP_M M-tiles before the next N-tile so that the
 // XCD's L2 serves both operands' tiles to several workgroups.
-__device__ __forceinline__ int xcd_logical(int nwg) {
+__device__ __forceinline__ int xcd_logical_of(int pid, int nwg) {
   constexpr int NXCD = 8;
-  const int pid = blockIdx.x;
   const int q = nwg / NXCD, rem = nwg % NXCD;
   const int x = pid % NXCD;
   return x * q + (x < rem ? x : rem) + pid / NXCD;
 }
+__device__ __forceinline__ int xcd_logical(int nwg) { return xcd_logical_of((int)blockIdx.x, nwg); }
 template <int GROUP_M = 8>
 __device__ __forceinline__ void group_tile(int logical, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int in_group = GROUP_M * tiles_n;

@@ -501,9 +501,72 @@ template <class TL>
 constexpr int orms_off() {
   return (epi_area_bytes<TL>() + 1023) / 1024 * 1024;
 }
+
+// Persistent workgroups: the 8-wave one-pair and block-diagonal tiles of the
+// storing epilogues run one workgroup per CU that walks its tiles. Once a
+// tile's main loop is done, the next tile's first K-tiles (the loads the
+// prologue issues before its barrier) go into their stages while the
+// epilogue runs from LDS areas outside them; the launch gap, the argument
+// loads and the pipeline fill of every tile but the first then overlap the
+// epilogue's stores.
+// (The Online RMSNorm tile, at 256 VGPRs, would spill with the tile loop's
+// state, and its long-K launches have few tiles per CU.)
+template <class TL, int NPAIR, int EPI>
+constexpr bool gemm2_persist() {
+  return TL::NWAVE == 8 && TL::NSPLIT == 1 &&
+         (EPI == EPI_STORE || EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD2) &&
+         (TL::BDIAG || (NPAIR == 1 && TL::BM == 256 && TL::BN == 256));
+}
+
+// LDS places of the epilogue: the staging bands (and the RMSNorm-backward
+// column sums after them), the Online RMSNorm row totals and scales, and the
+// band-input slots, slot p of wave w at slot_off(p) + w * NIN * 2 KB.
+// Without persistence they start at the ring's origin. With it they avoid
+// the stages that hold the next tile's first K-tiles: shared ring, stages
+// 0 .. NSTAGE - 2 (the areas follow them); separate rings, A stages 0 and 1
+// and B stage 0 (staging and row sums in B stage 1, slots 0 and 1 in A
+// stage 2, slot 2 in the rest of B stage 1).
+template <class TL, int NPAIR, int EPI>
+struct EpiLds {
+  static constexpr bool P = gemm2_persist<TL, NPAIR, EPI>();
+  static constexpr int NIN = epi_nin<EPI>();
+  static constexpr int EW = TL::NWAVE * epi_wave_bytes<TL>();
+  static constexpr int SLOT = TL::NWAVE * NIN * 2048;  // one slot of every wave
+  static constexpr int AB = TL::BM * TL::BK * 2, BB = TL::BNO * TL::BK * 2;
+  static constexpr int ST = !P ? 0 : TL::ASYM ? TL::NSTAGE_A * AB + BB
+                                              : (TL::NSTAGE - 1) * stage_bytes<TL, NPAIR>();
+  static constexpr int ORM = !P ? orms_off<TL>() : ST + EW;
+  static constexpr int RS = EPI == EPI_ORMS ? 8 * TL::BM : 0;  // row totals and scales
+  static constexpr int IN0 = !P ? epi_in0<TL, EPI>() : TL::ASYM ? 2 * AB : ST + EW + RS;
+  static constexpr int LDS_MAX = 160 * 1024;
+  static constexpr int PDS0 = epi_pds<TL, EPI>();
+  static constexpr int PDS_FIT = SLOT ? (LDS_MAX - IN0) / SLOT : PDS0;
+  static constexpr int PDS = !P ? PDS0 : TL::ASYM ? (PDS0 < 3 ? PDS0 : 3)
+                                       : (PDS0 < PDS_FIT ? PDS0 : PDS_FIT);
+  static constexpr int slot_off(int p) {
+    return (P && TL::ASYM && p == 2) ? ST + EW : IN0 + p * SLOT;
+  }
+  static constexpr int end_() {
+    int e = ST + EW + RS;
+    for (int p = 0; p < (NIN ? PDS : 0); ++p) e = slot_off(p) + SLOT > e ? slot_off(p) + SLOT : e;
+    return e;
+  }
+  static constexpr int END = end_();
+  static_assert(!P || NIN == 0 || PDS >= 2, "persistent epilogue needs two band-input slots");
+  static_assert(!P || !TL::ASYM || (TL::NSTAGE_A == 3 && TL::NSTAGE == 2 && AB >= 2 * SLOT &&
+                                    BB >= EW + (RS > SLOT ? RS : SLOT)),
+                "separate-ring epilogue places");
+  static_assert(!P || END <= LDS_MAX, "persistent epilogue areas exceed LDS");
+};
+
 template <class TL, int NPAIR, int EPI>
 constexpr int gemm2_lds_bytes() {
-  return gemm2_body_bytes<TL, NPAIR, EPI>();
+  if constexpr (gemm2_persist<TL, NPAIR, EPI>()) {
+    constexpr int ring = ring_bytes<TL, NPAIR>(), e = EpiLds<TL, NPAIR, EPI>::END;
+    return ring > e ? ring : e;
+  } else {
+    return gemm2_body_bytes<TL, NPAIR, EPI>();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -533,10 +596,13 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   constexpr int XCH = epi_xch_bytes<TL, EPI>();
   constexpr int IN0 = epi_in0<TL, EPI>();
   constexpr int BODY = gemm2_body_bytes<TL, NPAIR, EPI>();
+  using EL = EpiLds<TL, NPAIR, EPI>;
+  constexpr bool PST = EL::P;
+  constexpr int LDSB = gemm2_lds_bytes<TL, NPAIR, EPI>();
   // Online RMSNorm, after the main loop: per-row sums of squares, row scales.
-  float* sTot = reinterpret_cast<float*>(lds + orms_off<TL>());  // [BM]
+  float* sTot = reinterpret_cast<float*>(lds + EL::ORM);  // [BM]
   float* sRow = sTot + BM;                                      // [BM]
-  static_assert(!ORMS || orms_off<TL>() + 8 * BM <= BODY, "row sums exceed the ring");
+  static_assert(!ORMS || EL::ORM + 8 * BM <= LDSB, "row sums exceed the ring");
 
   // The wave index is uniform across a wave: keep it in a scalar register.
   const int tid = threadIdx.x, lane = tid & 63;
@@ -567,7 +633,19 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     M = g.M;
     N = g.N;
   }
-  const int m0 = tm * BM, n0 = tn * BNO;
+  // Persistent launches: tile v of tiles_m x tiles_n x groups (the groups
+  // after one another), through the same XCD remapping with v in place of
+  // the workgroup id (the grid is a multiple of 8 whenever a workgroup runs
+  // more than one tile, so v and its workgroup sit on the same XCD).
+  int vt = (int)blockIdx.x;
+  auto vcoords = [&](int vv, int& tm_, int& tn_, int& slot_) {
+    const int tmn = g.tiles_m * g.tiles_n;
+    const int lg = xcd_logical_of(vv, g.vtiles);
+    slot_ = NPAIR == 1 ? lg / tmn : 0;
+    group_tile<4>(lg - slot_ * tmn, g.tiles_m, g.tiles_n, tm_, tn_);
+  };
+  if constexpr (PST) vcoords(vt, tm, tn, slot);
+  int m0 = tm * BM, n0 = tn * BNO;
   const int split = (int)blockIdx.z / g.groups;
 
   // With two waves per SIMD the SIMD serves the older wave's MFMAs first,
@@ -599,37 +677,38 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   const bf16_t* pb[3];
   int64_t sa[3], sb[3];  // element step of the source pointer per K-tile
   int64_t ea[3], eb[3];  // elements of the operand from pa / pb on
-  {
-    const int p0 = slot;
+  // The operands' loaders for the tile at rows m0_, columns n0_ of slot_.
+  auto init_ops = [&](int m0_, int n0_, int M_, int N_, int slot_) {
+    const int p0 = slot_;
     // Selected with constant indices (not g.a[p0]): a run-time index into
     // the argument arrays would go through private memory, and the values
     // would no longer be known to be the same in every lane.
     pa[0] = static_cast<const bf16_t*>(pick3(g.a, p0));
     pb[0] = static_cast<const bf16_t*>(pick3(g.b, p0));
     const int64_t lda0 = pick3(g.lda, p0), ldb0 = pick3(g.ldb, p0);
-    a0.init(lda0, m0, M, lane, wave);
-    b0.init(ldb0, n0, N, lane, wave);
-    ea[0] = OA0::extent(lda0, M, g.K);
-    eb[0] = OB0::extent(ldb0, N, g.K);
+    a0.init(lda0, m0_, M_, lane, wave);
+    b0.init(ldb0, n0_, N_, lane, wave);
+    ea[0] = OA0::extent(lda0, M_, g.K);
+    eb[0] = OB0::extent(ldb0, N_, g.K);
     sa[0] = (MCMASK & 1u) ? (int64_t)BK * lda0 : BK;
     sb[0] = (MCMASK & 2u) ? (int64_t)BK * ldb0 : BK;
     if constexpr (NPAIR > 1) {
       pa[1] = static_cast<const bf16_t*>(g.a[1]);
       pb[1] = static_cast<const bf16_t*>(g.b[1]);
-      a1.init(g.lda[1], m0, M, lane, wave);
-      b1.init(g.ldb[1], n0, N, lane, wave);
-      ea[1] = OA1::extent(g.lda[1], M, g.K);
-      eb[1] = OB1::extent(g.ldb[1], N, g.K);
+      a1.init(g.lda[1], m0_, M_, lane, wave);
+      b1.init(g.ldb[1], n0_, N_, lane, wave);
+      ea[1] = OA1::extent(g.lda[1], M_, g.K);
+      eb[1] = OB1::extent(g.ldb[1], N_, g.K);
       sa[1] = (MCMASK & 4u) ? (int64_t)BK * g.lda[1] : BK;
       sb[1] = (MCMASK & 8u) ? (int64_t)BK * g.ldb[1] : BK;
     }
     if constexpr (NPAIR > 2) {
       pa[2] = static_cast<const bf16_t*>(g.a[2]);
       pb[2] = static_cast<const bf16_t*>(g.b[2]);
-      a2.init(g.lda[2], m0, M, lane, wave);
-      b2.init(g.ldb[2], n0, N, lane, wave);
-      ea[2] = OA2::extent(g.lda[2], M, g.K);
-      eb[2] = OB2::extent(g.ldb[2], N, g.K);
+      a2.init(g.lda[2], m0_, M_, lane, wave);
+      b2.init(g.ldb[2], n0_, N_, lane, wave);
+      ea[2] = OA2::extent(g.lda[2], M_, g.K);
+      eb[2] = OB2::extent(g.ldb[2], N_, g.K);
       sa[2] = (MCMASK & 16u) ? (int64_t)BK * g.lda[2] : BK;
       sb[2] = (MCMASK & 32u) ? (int64_t)BK * g.ldb[2] : BK;
     }
@@ -643,7 +722,8 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       ea[p] -= kt0 * sa[p];
       eb[p] -= kt0 * sb[p];
     }
-  }
+  };
+  init_ops(m0, n0, M, N, slot);
   auto stage_ptr = [&](int s) { return lds + s * SB; };
   // Stage tiles of K-tile kt: [A][B] stages, or the two rings.
   auto a_stage = [&](int kt) {
@@ -743,7 +823,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   for (int i = 0; i < FSS; ++i) ssp[i] = tot[i] = 0.f;
   // Per-panel sums are written as each panel ends (by the first column tile
   // of a row band only) unless the caller asked for the total.
-  const bool ss_panels = ORMS && g.ss_out != nullptr && !g.emit_partial && tn == 0;
+  bool ss_panels = ORMS && g.ss_out != nullptr && !g.emit_partial && tn == 0;
   int panel = 0, in_panel = 0;
 
   // Fragment registers are double-buffered: the LDS reads of sub-step q + 1
@@ -829,21 +909,39 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   static_assert(!TL::ASYM || (SA == 3 && S == 2), "separate rings: 3 A stages, 2 B stages");
   constexpr int LA = OA0::PER;
   static_assert(!TL::ASYM || 2 * LA + OB0::PER < 64, "too many loads in flight for vmcnt");
-  if constexpr (TL::ASYM) {
-    issue_a(0);
-    issue_b(0);
-    issue_a(1);
-    wait_vmcnt<LA>();
-    block_barrier();
-    issue_b(1);
-    issue_a(2);
-  } else {
+  // The prologue: the loads issued before its barrier (pro_pre), then the
+  // wait for K-tile 0, the barrier and the loads of the stages it frees
+  // (pro_post). A persistent workgroup runs the next tile's pro_pre before
+  // the epilogue and its pro_post after; AF is the number of vector-memory
+  // operations the wave issued in between (a lower bound: waiting for
+  // fewer in flight is never too early), which may still be in flight
+  // since operations retire in order.
+  auto pro_pre = [&]() {
+    if constexpr (TL::ASYM) {
+      issue_a(0);
+      issue_b(0);
+      issue_a(1);
+    } else {
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s) issue(s);
-    wait_vmcnt<VM_AFTER>();
+      for (int s = 0; s < S - 1; ++s) issue(s);
+    }
+  };
+  auto pro_post = [&](auto after_tag) {
+    constexpr int W = (TL::ASYM ? LA : VM_AFTER) + decltype(after_tag)::value;
+    wait_vmcnt<(W < 63 ? W : 63)>();
+    wait_lgkmcnt0();  // every wave's epilogue is done with its LDS areas
     block_barrier();
-    issue(S - 1);
-  }
+    if constexpr (TL::ASYM) {
+      issue_b(1);
+      issue_a(2);
+    } else {
+      issue(S - 1);
+    }
+  };
+  pro_pre();
+  pro_post(std::integral_constant<int, 0>{});
+
+  for (;;) {  // the tiles of a persistent workgroup (one otherwise)
   read_q(0, stage_ptr(0), 0, 0);
   // Fragment reads are in flight only inside the loop body, between a
   // sub-step's start and the next sub-step's wait: every path into and out
@@ -946,6 +1044,18 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       if (i % TL::NWN == wn && lane < 16) sTot[w0m + 16 * i + lane] = tot[i / TL::NWN];
     __syncthreads();
   }
+  // Persistent: the next tile's coordinates, loaders and first loads; the
+  // epilogue's LDS areas lie outside the stages these fill.
+  bool more = false;
+  int tm1 = 0, tn1 = 0, slot1 = 0;
+  if constexpr (PST) {
+    if (vt + (int)gridDim.x < g.vtiles) {
+      more = true;
+      vcoords(vt + (int)gridDim.x, tm1, tn1, slot1);
+      init_ops(tm1 * BM, tn1 * BNO, M, N, slot1);
+      pro_pre();
+    }
+  }
 
   // Epilogue geometry. Split tiles: the wave running pair 0 (gate) and its
   // partner in the same row band running pair 1 (up) each finish half of the
@@ -960,9 +1070,12 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   // The MFMA takes the B fragment as its first operand, so fragment (i, j)
   // of lane l holds row rb + 16 i + (l & 15) of the block tile at the four
   // consecutive columns cb + 16 j + 4 (l >> 4) + v, v = 0..3.
-  // (The lane index is recomputed here so that the compiler does not keep
-  // values derived from it alive across the main loop.)
-  const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  // (The lane index is recomputed here, behind an empty asm statement the
+  // compiler cannot move, so that it keeps no values derived from it alive
+  // across the main loop, nor hoists them out of a persistent tile loop.)
+  int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(elane));
+  const int lane = elane;  // the epilogue's lane index
   const int fr = elane & 15, fc = 4 * (elane >> 4);
 
   // HBM inputs of the epilogue, requested before anything else: gamma and
@@ -973,10 +1086,10 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   constexpr bool HAS_GAMMA = (EPI == EPI_RMSBWD || EPI == EPI_WGRAD);
   constexpr bool HAS_ROW = (EPI == EPI_STORE || EPI == EPI_RMSBWD);
   constexpr int NIN = (HAS_RES ? 1 : 0) + (HAS_H ? 1 : 0);
-  constexpr int PDS = epi_pds<TL, EPI>();
+  constexpr int PDS = EL::PDS;
   static_assert(NIN == epi_nin<EPI>(), "input count");
   static_assert(NIN == 0 || TL::WTN == 64, "band inputs need 64-column wave tiles");
-  static_assert(NIN == 0 || IN0 + TL::NWAVE * PDS * NIN * 2048 <= BODY, "input slots exceed LDS");
+  static_assert(NIN == 0 || EL::slot_off(PDS - 1) + EL::SLOT <= LDSB, "input slots exceed LDS");
   const bf16_t* resp = static_cast<const bf16_t*>(g.res);
   const bf16_t* hp = static_cast<const bf16_t*>(g.hsrc);
 
@@ -1023,11 +1136,11 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   EpiDma in_res, in_h;
   if constexpr (HAS_RES) in_res.init(resp, g.ldres, m0, n0, M, N, rb, cb, lane);
   if constexpr (HAS_H) in_h.init(hp, g.ldh, m0, n0, M, N, rb, cb, lane);
-  unsigned char* sIn = lds + IN0 + wave * (PDS * NIN * 2048);  // [PDS][NIN][2 KB]
+  unsigned char* sIn = lds + wave * (NIN * 2048);  // + slot_off(p): [NIN][2 KB]
   // A plain store without a residual has no band inputs.
   const bool in_on = NIN > 0 && (EPI != EPI_STORE || resp != nullptr);
   auto issue_band = [&](int i) {
-    unsigned char* slot = sIn + (i % PDS) * (NIN * 2048);
+    unsigned char* slot = sIn + EL::slot_off(i % PDS);
     if constexpr (HAS_RES) in_res.issue(i, slot);
     if constexpr (HAS_H) in_h.issue(i, slot + 2048);
   };
@@ -1050,7 +1163,14 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
         if (g.ss_out && g.emit_partial) g.ss_out[gr] = ss;
       }
     }
-    __syncthreads();
+    if constexpr (PST) {
+      // A bare barrier: __syncthreads would also wait for the next tile's
+      // loads in flight.
+      wait_lgkmcnt0();
+      block_barrier();
+    } else {
+      __syncthreads();
+    }
   }
 
   if constexpr (SPLITN) {
@@ -1129,7 +1249,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   constexpr int CH = TL::WTN / 8;     // 16-byte chunks per row
   constexpr int PERL = 16 * CH / 64;  // chunks per lane per band
   auto swz_st = [](int row) { return RB == 128 ? epi_swz(row) : ((row >> 2) & 3); };
-  unsigned char* sWb = lds + wave * epi_wave_bytes<TL>();
+  unsigned char* sWb = lds + EL::ST + wave * epi_wave_bytes<TL>();
   constexpr int NOUT = (EPI == EPI_SWIGLU_BWD || EPI == EPI_SWIGLU_BWD2) ? 3 : 1;
   void* cq[NOUT];
   int64_t lq[NOUT];
@@ -1138,7 +1258,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   for (int q = 0; q < NOUT; ++q) {
     cq[q] = (EPI == EPI_STORE) ? pick3(g.c, slot) : pick3(g.c, q);
     lq[q] = (EPI == EPI_STORE) ? pick3(g.ldc, slot) : pick3(g.ldc, q);
-    if constexpr (NIN > 0) outs[q].init(cq[q], lq[q], m0, n0, M, N, rb, cb, lane, CH);
+    if constexpr (NIN > 0 || PST) outs[q].init(cq[q], lq[q], m0, n0, M, N, rb, cb, lane, CH);
   }
   // With band inputs in flight every lane must issue the same stores (the
   // waits count them), so they go through the buffer range check; without,
@@ -1204,7 +1324,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
         sched_fence();
         wait_vmcnt_le(after);
         sched_fence();
-        const unsigned char* slot = sIn + (i % PDS) * (NIN * 2048);
+        const unsigned char* slot = sIn + EL::slot_off(i % PDS);
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           if constexpr (HAS_RES) rin[j] = *reinterpret_cast<const u32x2*>(slot + epi_acc_off(j, lane));
@@ -1265,7 +1385,8 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
         }
       }
 #pragma unroll
-      for (int q = 0; q < NOUT; ++q) put_band(i, pk[q], outs[q], cq[q], lq[q], in_tag);
+      for (int q = 0; q < NOUT; ++q)
+        put_band(i, pk[q], outs[q], cq[q], lq[q], std::integral_constant<bool, IN || PST>{});
     }
   };
   if constexpr (EPI != EPI_WGRAD) {
@@ -1296,7 +1417,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
         x += __shfl_xor(x, 8, 64);
         colacc[j][v] = x;
       }
-    float* sCol = reinterpret_cast<float*>(lds + TL::NWAVE * epi_wave_bytes<TL>());  // [NWM][BN]
+    float* sCol = reinterpret_cast<float*>(lds + EL::ST + EL::EW);  // [NWM][BN]
     if (fr == 0) {
 #pragma unroll
       for (int j = 0; j < FN; ++j)
@@ -1326,7 +1447,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   }
 
   if constexpr (EPI == EPI_RMSBWD) {
-    const float* sCol = reinterpret_cast<const float*>(lds + TL::NWAVE * epi_wave_bytes<TL>());
+    const float* sCol = reinterpret_cast<const float*>(lds + EL::ST + EL::EW);
     // A bare barrier: the column sums are in LDS; the band stores may
     // still be in flight.
     wait_lgkmcnt0();
@@ -1355,6 +1476,40 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       if (lane == 0) g.cs_out[c] = sum;
     }
   }
+
+  if (!more) break;
+  // The next tile. The vector-memory operations this wave issued after the
+  // next tile's first loads: the row scalars, the band inputs and the
+  // stores (uniform in a persistent workgroup), a count known per path.
+  vt += (int)gridDim.x;
+  tm = tm1;
+  tn = tn1;
+  slot = slot1;
+  m0 = tm * BM;
+  n0 = tn * BNO;
+  // The loaders again (a few scalar and vector operations): their values
+  // from before the epilogue need not stay live across it.
+  init_ops(m0, n0, M, N, slot);
+  if constexpr (ORMS) ss_panels = g.ss_out != nullptr && !g.emit_partial && tn == 0;
+#pragma unroll
+  for (int p = 0; p < NACC; ++p)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[p][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < FSS; ++i) ssp[i] = tot[i] = 0.f;
+  panel = 0;
+  in_panel = 0;
+  {
+    constexpr int E_OUT = (HAS_ROW ? FME : 0) + FME * NOUT * PERL;
+    constexpr int E_IN = E_OUT + FME * 2 * NIN;
+    if (in_on)
+      pro_post(std::integral_constant<int, E_IN>{});
+    else
+      pro_post(std::integral_constant<int, E_OUT>{});
+  }
+  }  // tiles
 #undef LR_E
 }
 

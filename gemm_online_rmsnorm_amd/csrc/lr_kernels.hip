@@ -2,6 +2,7 @@
 // memory-bound helpers (gamma folding, r-wide row dots, column reductions,
 // rank-share finalisation).
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "lr_common.hpp"
@@ -138,6 +139,19 @@ using PBD256x128 = Tile2<256, 128, 64, 4, 2, 3, 1, 0, 1>;
 #define LR_SWIGLU_TILE 1
 #endif
 
+// Compute units of the current device (looked up once per device).
+static int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <class TL, int NPAIR, uint32_t MC, int EPI>
 static hipError_t launch2(const GemmDesc& d, int groups, hipStream_t s) {
   auto kern = gemm2_kernel<TL, NPAIR, MC, EPI>;
@@ -188,9 +202,22 @@ static hipError_t launch2(const GemmDesc& d, int groups, hipStream_t s) {
   g.cs_n = d.cs_n;
   g.cs_out = d.cs_out;
   if (g.tiles_m == 0 || g.tiles_n == 0 || groups == 0) return hipSuccess;
-  dim3 grid(g.tiles_m * g.tiles_n, 1, groups * split);
-  hipLaunchKernelGGL(kern, grid, dim3(TL::NT), lds, s, g);
-  return hipGetLastError();
+  if constexpr (gemm2_persist<TL, NPAIR, EPI>()) {
+    // One workgroup per CU walks the tiles; a multiple of 8 workgroups
+    // whenever one runs several, so that a tile keeps its XCD.
+    if (split != 1) return hipErrorInvalidValue;
+    const int64_t total = (int64_t)g.tiles_m * g.tiles_n * groups;
+    if (total > INT32_MAX) return hipErrorInvalidValue;
+    const int64_t ncu = device_cus() / 8 * 8;
+    g.vtiles = (int)total;
+    const int nwg = (int)(total > ncu && ncu > 0 ? ncu : total);
+    hipLaunchKernelGGL(kern, dim3(nwg), dim3(TL::NT), lds, s, g);
+    return hipGetLastError();
+  } else {
+    dim3 grid(g.tiles_m * g.tiles_n, 1, groups * split);
+    hipLaunchKernelGGL(kern, grid, dim3(TL::NT), lds, s, g);
+    return hipGetLastError();
+  }
 }
 
 static int64_t ntiles(const GemmDesc& d, int bm, int bn, int groups) {
