@@ -1366,11 +1366,14 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
           } else if constexpr (EPI == EPI_SWIGLU_BWD2) {
             // g, u recomputed in the accumulators, dm from HBM:
             // m = SiLU(g) u; dg = dm u sig(g)(1 + g(1 - sig(g))); du = dm SiLU(g)
+            // (SiLU'(g) = sig(g) + SiLU(g) (1 - sig(g)): one FMA on values
+            // already at hand; the epilogue is bound by its vector work.)
             const float uu = LR_E(1, i, j)[v], dm = rv[v];
             const float sg = sigmoid_f<bf16_t>(x);
             const float sl = x * sg;
+            const float ds = __builtin_fmaf(sl, 1.0f - sg, sg);
             o[0][v] = sl * uu;
-            o[1][v] = dm * uu * sg * (1.0f + x * (1.0f - sg));
+            o[1][v] = (dm * uu) * ds;
             o[2][v] = dm * sl;
           }
         }
