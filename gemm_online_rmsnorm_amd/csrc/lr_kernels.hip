@@ -393,24 +393,43 @@ int gemm_tile_m_used(int op, int dtype, const GemmDesc& d, int groups) {
 }
 
 // out[slot][i, j] = colscale[j] * sum_s part[s][slot][i, j], s in order.
+// The outputs of the groups of one grouped weight gradient.
+struct SumOut {
+  float* out[3];
+  int64_t ldo[3];
+};
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                             int splits, int64_t split_stride,
-                                                            int64_t count, int n,
+                                                            int64_t count, int groups, int n,
                                                             const bf16_t* __restrict__ colscale,
-                                                            float* __restrict__ out, int64_t ldo) {
+                                                            SumOut o) {
+  // part holds groups x count floats per slice (group g at g * count), the
+  // slices split_stride apart; group g's sum goes to o.out[g].
   const int64_t nq = count / 4;
-  for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < nq;
+  for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < nq * groups;
        q += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t e = q * 4;
-    f32x4 acc = *reinterpret_cast<const f32x4*>(part + e);
-    for (int sp = 1; sp < splits; ++sp)
-      acc += *reinterpret_cast<const f32x4*>(part + sp * split_stride + e);
+    const int g = (int)(q / nq);
+    const int64_t e = (q - g * nq) * 4;
+    const float* pg = part + g * count;
+    // Slices in order 0, 1, 2, ...; four loads in flight at a time.
+    f32x4 acc = *reinterpret_cast<const f32x4*>(pg + e);
+    int sp = 1;
+    for (; sp + 3 < splits; sp += 4) {
+      f32x4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const f32x4*>(pg + (sp + k) * split_stride + e);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc += v[k];
+    }
+    for (; sp < splits; ++sp) acc += *reinterpret_cast<const f32x4*>(pg + sp * split_stride + e);
     const int64_t row = e / n;
     const int col = (int)(e % n);
     if (colscale) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) acc[k] *= Elem<bf16_t>::load(colscale + col + k);
     }
+    float* out = g == 0 ? o.out[0] : (g == 1 ? o.out[1] : o.out[2]);
+    const int64_t ldo = g == 0 ? o.ldo[0] : (g == 1 ? o.ldo[1] : o.ldo[2]);
     *reinterpret_cast<f32x4*>(out + row * ldo + col) = acc;
   }
 }
@@ -446,18 +465,19 @@ hipError_t run_wgrad_gemm(int dtype, const GemmDesc& d, int groups, int splits, 
 
 hipError_t run_wgrad_sum(const GemmDesc& d, int groups, int splits, const void* part,
                          hipStream_t s) {
+  if (groups < 1 || groups > 3) return hipErrorInvalidValue;
   const int64_t mn = (int64_t)d.M * d.N;
-  const float* pbase = static_cast<const float*>(part);
+  SumOut o{};
   for (int gidx = 0; gidx < groups; ++gidx) {
-    const int64_t nq = mn / 4;
-    int grid = (int)std::min<int64_t>((nq + 255) / 256, 8192);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, s, pbase + gidx * mn,
-                       splits, groups * mn, mn, d.N, static_cast<const bf16_t*>(d.colscale),
-                       static_cast<float*>(d.c[gidx]), d.ldc[gidx]);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    o.out[gidx] = static_cast<float*>(d.c[gidx]);
+    o.ldo[gidx] = d.ldc[gidx];
   }
-  return hipSuccess;
+  const int64_t nq = mn / 4 * groups;
+  const int grid = (int)std::min<int64_t>((nq + 255) / 256, 8192);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, s,
+                     static_cast<const float*>(part), splits, groups * mn, mn, groups, d.N,
+                     static_cast<const bf16_t*>(d.colscale), o);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -677,15 +697,15 @@ __global__ __launch_bounds__(256) void finalize_kernel(const T* __restrict__ P, 
                                                        int width, float inv_D, float eps,
                                                        T* __restrict__ z, int64_t ldz,
                                                        float* __restrict__ rms_out) {
+  // One 16-byte chunk per thread: blockIdx.x picks 256 chunks of a row,
+  // blockIdx.y (stepping by gridDim.y) the row, so every load is independent.
   constexpr int VEC = Elem<T>::VEC;
-  const int lane = threadIdx.x & 63;
-  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int nwaves = (gridDim.x * blockDim.x) >> 6;
-  for (int t = wave; t < rows; t += nwaves) {
+  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * VEC;
+  for (int t = blockIdx.y; t < rows; t += gridDim.y) {
     const float rmsg = sqrtf(ss[t] * inv_D + eps);
-    const float s = 1.0f / rmsg;
-    if (lane == 0 && rms_out) rms_out[t] = rmsg;
-    for (int c = lane * VEC; c < width; c += 64 * VEC) {
+    if (c == 0 && rms_out) rms_out[t] = rmsg;
+    if (c < width) {
+      const float s = 1.0f / rmsg;
       float x[VEC];
       unpack16<T>(*reinterpret_cast<const u32x4*>(P + (int64_t)t * ldp + c), x);
 #pragma unroll
@@ -756,13 +776,15 @@ hipError_t run_colsum(const float* part, int tiles, int n, float* out, hipStream
 hipError_t run_finalize(int dtype, const void* P, int64_t ldp, const float* ss, int rows,
                         int width, float inv_D, float eps, void* z, int64_t ldz, float* rms_out,
                         hipStream_t s) {
-  const int grid = grid_for(rows, 4);
+  if (rows <= 0) return hipSuccess;
+  const int vec = dtype == 0 ? 4 : 8;
+  const dim3 grid((unsigned)std::max(1, (width / vec + 255) / 256), (unsigned)std::min(rows, 65535));
   if (dtype == 0) {
-    hipLaunchKernelGGL(finalize_kernel<float>, dim3(grid), dim3(256), 0, s,
+    hipLaunchKernelGGL(finalize_kernel<float>, grid, dim3(256), 0, s,
                        static_cast<const float*>(P), ldp, ss, rows, width, inv_D, eps,
                        static_cast<float*>(z), ldz, rms_out);
   } else {
-    hipLaunchKernelGGL(finalize_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
+    hipLaunchKernelGGL(finalize_kernel<bf16_t>, grid, dim3(256), 0, s,
                        static_cast<const bf16_t*>(P), ldp, ss, rows, width, inv_D, eps,
                        static_cast<bf16_t*>(z), ldz, rms_out);
   }
