@@ -63,10 +63,13 @@ def test_grouped_gemm_layouts(dtype, layout, G, K):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("layout", ["NT", "NN"])
-@pytest.mark.parametrize("shape", [(264, 136, 72), (264, 136, 64), (4088, 4040, 64)])
+@pytest.mark.parametrize("shape", [(264, 136, 72), (264, 136, 64), (4088, 4040, 64),
+                                   (4360, 4040, 64)])
 def test_gemm_epilogues(dtype, layout, shape):
-    """Residual and row-scale epilogues; the last shape runs 256 x 256 tiles
-    with a partial last row band and a partial last column tile."""
+    """Plain, residual and row-scale epilogues; the last two shapes run
+    256 x 256 tiles with a partial last row band and a partial last column
+    tile, the last one 288 of them, so that the persistent workgroups (one
+    per CU) run a second tile, ragged, after a first one."""
     torch = gpu_or_skip()
     import gemm_online_rmsnorm_amd as lr
     rng = np.random.default_rng(7 + shape[2])
@@ -88,9 +91,15 @@ def test_gemm_epilogues(dtype, layout, shape):
     rsd = torch.from_numpy(rs).cuda()
     lr.grouped_lowrank_gemm([dict(M=M, N=N, K=K, X=X, W=Wd, Y=y2, aux=rsd)], dl, LAYOUT[layout],
                             lr.LR_EPI_ROW_SCALE)
+    # plain
+    y3 = torch.empty(M, N, dtype=odt, device="cuda")
+    lr.grouped_lowrank_gemm([dict(M=M, N=N, K=K, X=X, W=Wd, Y=y3)], dl, LAYOUT[layout],
+                            lr.LR_EPI_NONE)
     torch.cuda.synchronize()
+    say(f"[case] epilogues {layout} {dtype} {shape}")
     assert rel_err(_host(y), op.grouped_gemm(layout, [(x, w)], "residual", res)[0]) <= tol
     assert rel_err(_host(y2), op.grouped_gemm(layout, [(x, w)], "row_scale", rs)[0]) <= tol
+    assert rel_err(_host(y3), op.grouped_gemm(layout, [(x, w)])[0]) <= tol
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
