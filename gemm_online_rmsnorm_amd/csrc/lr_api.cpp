@@ -213,7 +213,23 @@ struct BwdWs {
   float *coef1, *coef2, *colpart;
   void* wpart;         // split-K partials of the weight gradients
   size_t wpart_bytes;
+  // Transposed copies of the weights the data gradients multiply by (null
+  // when the shape does not allow them): B_dn^T [r, d], A_dn^T [F, r],
+  // B_g^T, B_u^T [r, F], A_gu^T [d, 2r], B_o^T [r, d], A_o^T [d, r],
+  // B_q^T, B_k^T, B_v^T [r, d], A_qkv^T [d, 3r].
+  void *tB_dn, *tA_dn, *tB_g, *tB_u, *tA_gu, *tB_o, *tA_o, *tB_q, *tB_k, *tB_v, *tA_qkv;
 };
+
+// The backward's data-gradient products multiply an activation gradient by a
+// weight whose rows run along the output (NN). On the pipelined engine they
+// run as NT products against transposed copies of their weights, made once
+// per call in one launch per stage: the NN tiles' transposing LDS reads cost
+// 3-10% at these shapes (measured against NT with the transposed weight).
+// The copies need bf16 and every side a multiple of 64 (whole tiles of the
+// transpose kernel and whole k-tiles of the products).
+bool transposed_weights(const lr_block_shape* s) {
+  return s->dtype == LR_BF16 && s->d % 64 == 0 && s->r % 64 == 0 && s->d_ff % 64 == 0;
+}
 
 // A weight-gradient (TN) descriptor: out [M, N] = a^T b over K rows.
 lr::GemmDesc tn_desc(int M, int N, int K, const void* a, int64_t lda, const void* b, int64_t ldb,
@@ -308,6 +324,20 @@ size_t carve_bwd(const lr_block_shape* s, void* base, BwdWs* out) {
   w.colpart = static_cast<float*>(c.take(4 * tiles * s->d));
   w.wpart_bytes = wgrad_part_max(s);
   w.wpart = c.take(w.wpart_bytes);
+  const bool tw = transposed_weights(s);
+  const int64_t d = s->d, r = s->r, F = s->d_ff;
+  auto tk = [&](int64_t n) { return tw ? c.take(e * n) : nullptr; };
+  w.tB_dn = tk(r * d);
+  w.tA_dn = tk(F * r);
+  w.tB_g = tk(r * F);
+  w.tB_u = tk(r * F);
+  w.tA_gu = tk(d * 2 * r);
+  w.tB_o = tk(r * d);
+  w.tA_o = tk(d * r);
+  w.tB_q = tk(r * d);
+  w.tB_k = tk(r * d);
+  w.tB_v = tk(r * d);
+  w.tA_qkv = tk(d * 3 * r);
   if (out) *out = w;
   return c.off + 256;
 }
@@ -329,6 +359,30 @@ int gemm(int op, int dtype, const lr::GemmDesc& d, int groups, hipStream_t st,
   hipError_t e = lr::run_gemm(op, dtype, d, groups, st);
   if (e != hipSuccess) return hip_fail(e, what);
   return LR_OK;
+}
+
+// A data-gradient product X W (NN, `nn`), or, with the transposed weights
+// `wt` (one per group, [N, K] rows), the same product as X wt^T (NT) when
+// the pipelined engine takes it. The operation and descriptor it ran go to
+// *op_run and *used.
+int nn_or_nt(int op_nn, int op_nt, int dtype, const lr::GemmDesc& nn, const void* const* wt,
+             int groups, hipStream_t st, const char* what, int* op_run = nullptr,
+             lr::GemmDesc* used = nullptr) {
+  if (wt != nullptr && wt[0] != nullptr) {
+    lr::GemmDesc g = nn;
+    for (int i = 0; i < groups; ++i) {
+      g.b[i] = wt[i];
+      g.ldb[i] = nn.K;
+    }
+    if (lr::uses_engine2(op_nt, dtype, g, groups)) {
+      if (op_run) *op_run = op_nt;
+      if (used) *used = g;
+      return gemm(op_nt, dtype, g, groups, st, what);
+    }
+  }
+  if (op_run) *op_run = op_nn;
+  if (used) *used = nn;
+  return gemm(op_nn, dtype, nn, groups, st, what);
 }
 
 // One weight-gradient GEMM (split-K through the workspace when it pays):
@@ -926,6 +980,17 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
   lr::GemmDesc last2[2] = {tn_desc(3 * r, d, T, W.dqs, 3 * r, X, d, gr->A_qkv, w->gamma1), dB_dn};
   const bool late_dbdn = stage == LR_STAGE_ALL && lr::wgrad_multi_ok(dt, last2, 2);
   if (post) {
+    if (W.tB_dn) {
+      const lr::TransposeJob jobs[7] = {
+          {w->B_dn, r, d, r, W.tB_dn, d},        {w->A_dn, F, r, F, W.tA_dn, r},
+          {w->B_g, r, F, r, W.tB_g, F},          {w->B_u, r, F, r, W.tB_u, F},
+          {w->A_gu, d, 2 * r, d, W.tA_gu, 2 * r}, {w->B_o, r, d, r, W.tB_o, d},
+          {w->A_o, d, r, d, W.tA_o, r}};
+      ProfScope ps("transpose B_dn, A_dn, B_g, B_u, A_gu, B_o, A_o", st,
+                   2.0 * e * r * (5.0 * d + 3.0 * F), true);
+      hipError_t he = launch_rep(ps, [&] { return lr::run_transpose_bf16(jobs, 7, st); });
+      if (he != hipSuccess) return hip_fail(he, "weight transposes");
+    }
     // dB_dn = dY^T d_r
     if (!late_dbdn) RUN(wgrad(dt, dB_dn, 1, W, st, "dB_dn", "dB_dn split-K sum"));
     // dd_r = dY B_dn
@@ -940,7 +1005,8 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.ldb[0] = r;
       g.c[0] = W.dd_r;
       g.ldc[0] = r;
-      RUN(gemm(lr::OP_NN_STORE, dt, g, 1, st, "dd_r"));
+      const void* wt[1] = {W.tB_dn};
+      RUN(nn_or_nt(lr::OP_NN_STORE, lr::OP_NT_STORE, dt, g, wt, 1, st, "dd_r"));
     }
     // Recompute g, u and dm = dd_r A_dn in one tile; m, dg, du out.
     {
@@ -986,7 +1052,8 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       two.ldres = F;
       if (lr::uses_engine2(lr::OP_NN_STORE, dt, dmg, 1) &&
           lr::uses_engine2(lr::OP_SWIGLU_BWD2, dt, two, 1)) {
-        RUN(gemm(lr::OP_NN_STORE, dt, dmg, 1, st, "dm = dd_r A_dn"));
+        const void* wt[1] = {W.tA_dn};
+        RUN(nn_or_nt(lr::OP_NN_STORE, lr::OP_NT_STORE, dt, dmg, wt, 1, st, "dm = dd_r A_dn"));
         RUN(gemm(lr::OP_SWIGLU_BWD2, dt, two, 1, st, "SwiGLU recompute + backward"));
       } else {
         RUN(gemm(lr::OP_SWIGLU_BWD, dt, g, 1, st, "SwiGLU recompute + backward"));
@@ -1045,7 +1112,8 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.c[1] = Bm(W.dgus, r, e);
       g.ldc[1] = 2 * r;
       g.rowdiv = sv->rms2;
-      RUN(gemm(lr::OP_NN_STORE, dt, g, 2, st, "dgu_r"));
+      const void* wt[2] = {W.tB_g, W.tB_u};
+      RUN(nn_or_nt(lr::OP_NN_STORE, lr::OP_NT_STORE, dt, g, wt, 2, st, "dgu_r"));
     }
     // coef2 = (dgus . gu_r) / (rms2 D)
     {
@@ -1091,8 +1159,12 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.colscale = w->gamma2;
       g.rowcoef = W.coef2;
       g.colsum = W.colpart;
-      RUN(gemm(lr::OP_NN_RMSBWD, dt, g, 1, st, "RMSNorm-2 backward"));
-      const int bm = lr::gemm_tile_m_used(lr::OP_NN_RMSBWD, dt, g, 1);
+      const void* wt[1] = {W.tA_gu};
+      int op_run = lr::OP_NN_RMSBWD;
+      lr::GemmDesc used;
+      RUN(nn_or_nt(lr::OP_NN_RMSBWD, lr::OP_NT_RMSBWD, dt, g, wt, 1, st, "RMSNorm-2 backward",
+                   &op_run, &used));
+      const int bm = lr::gemm_tile_m_used(op_run, dt, used, 1);
       cs_tiles = (T + bm - 1) / bm;
     }
     // do_r = dh B_o
@@ -1107,7 +1179,8 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.ldb[0] = r;
       g.c[0] = W.do_r;
       g.ldc[0] = r;
-      return gemm(lr::OP_NN_STORE, dt, g, 1, st, "do_r");
+      const void* wt[1] = {W.tB_o};
+      return nn_or_nt(lr::OP_NN_STORE, lr::OP_NT_STORE, dt, g, wt, 1, st, "do_r");
     };
     // dA_gu = gamma2 * (dgus^T h), dB_o = dh^T o_r, dA_o = do_r^T O. On the
     // pipelined engine the (first) launch also sums the RMSNorm backward's
@@ -1152,11 +1225,21 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.ldb[0] = d;
       g.c[0] = dO_attn;
       g.ldc[0] = d;
-      RUN(gemm(lr::OP_NN_STORE, dt, g, 1, st, "dO"));
+      const void* wt[1] = {W.tA_o};
+      RUN(nn_or_nt(lr::OP_NN_STORE, lr::OP_NT_STORE, dt, g, wt, 1, st, "dO"));
     }
   }
 
   if (pre) {
+    if (W.tB_q) {
+      const lr::TransposeJob jobs[4] = {{w->B_q, r, d, r, W.tB_q, d},
+                                        {w->B_k, r, d, r, W.tB_k, d},
+                                        {w->B_v, r, d, r, W.tB_v, d},
+                                        {w->A_qkv, d, 3 * r, d, W.tA_qkv, 3 * r}};
+      ProfScope ps("transpose B_q, B_k, B_v, A_qkv", st, 2.0 * e * 6.0 * r * d, true);
+      hipError_t he = launch_rep(ps, [&] { return lr::run_transpose_bf16(jobs, 4, st); });
+      if (he != hipSuccess) return hip_fail(he, "weight transposes");
+    }
     const void* dQKV[3] = {dQ, dK, dV};
     const void* Bs[3] = {w->B_q, w->B_k, w->B_v};
     float* dBs[3] = {gr->B_q, gr->B_k, gr->B_v};
@@ -1191,7 +1274,8 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
         g.ldc[i] = 3 * r;
       }
       g.rowdiv = sv->rms1;
-      RUN(gemm(lr::OP_NN_STORE, dt, g, 3, st, "dqkv_r"));
+      const void* wt[3] = {W.tB_q, W.tB_k, W.tB_v};
+      RUN(nn_or_nt(lr::OP_NN_STORE, lr::OP_NT_STORE, dt, g, wt, 3, st, "dqkv_r"));
     }
     // coef1 = (dqs . qkv_r) / (rms1 D)
     {
@@ -1221,8 +1305,12 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.colscale = w->gamma1;
       g.rowcoef = W.coef1;
       g.colsum = W.colpart;
-      RUN(gemm(lr::OP_NN_RMSBWD, dt, g, 1, st, "RMSNorm-1 backward"));
-      const int bm = lr::gemm_tile_m_used(lr::OP_NN_RMSBWD, dt, g, 1);
+      const void* wt[1] = {W.tA_qkv};
+      int op_run = lr::OP_NN_RMSBWD;
+      lr::GemmDesc used;
+      RUN(nn_or_nt(lr::OP_NN_RMSBWD, lr::OP_NT_RMSBWD, dt, g, wt, 1, st, "RMSNorm-1 backward",
+                   &op_run, &used));
+      const int bm = lr::gemm_tile_m_used(op_run, dt, used, 1);
       cs_tiles = (T + bm - 1) / bm;
     }
     // dA_qkv = gamma1 * (dqs^T X) (with dB_dn beside it when held back); on

@@ -18,7 +18,8 @@ enum GemmOp : int {
   OP_NN_RMSBWD = 5,   // RMSNorm backward epilogue + column sums
   OP_TN_WGRAD = 6,    // fp32 Y = X^T W [* colscale]            (grouped)
   OP_SWIGLU_BWD2 = 7, // NT, NT pairs (g, u) + dm from res -> m, dg, du (pipelined engine)
-  OP_COUNT = 8,
+  OP_NT_RMSBWD = 8,   // RMSNorm backward epilogue + column sums, NT (pipelined engine)
+  OP_COUNT = 9,
 };
 
 struct GemmDesc {
@@ -110,5 +111,19 @@ hipError_t run_colsum(const float* part, int tiles, int n, float* out, hipStream
 hipError_t run_finalize(int dtype, const void* P, int64_t ldp, const float* ss, int rows,
                         int width, float inv_D, float eps, void* z, int64_t ldz, float* rms_out,
                         hipStream_t s);
+
+// bf16 transposes out[c][r] = in[r][c] of up to kMaxTranspose matrices in
+// one launch (rows x cols each, leading dimensions ldi and ldo in elements).
+// Every row is whole 16-byte chunks (cols % 8 == 0) and every matrix whole
+// 64-row tiles (rows % 64 == 0); the caller checks.
+struct TransposeJob {
+  const void* in = nullptr;
+  int64_t ldi = 0;
+  int rows = 0, cols = 0;
+  void* out = nullptr;
+  int64_t ldo = 0;
+};
+constexpr int kMaxTranspose = 8;
+hipError_t run_transpose_bf16(const TransposeJob* jobs, int n, hipStream_t s);
 
 }  // namespace lr

@@ -244,6 +244,7 @@ static bool eligible2(int op, const GemmDesc& d, int groups, int bk) {
   switch (op) {
     case OP_NN_STORE:
     case OP_NN_RMSBWD: mc = 2u; break;
+    case OP_NT_RMSBWD: break;
     case OP_TN_WGRAD: mc = 3u; break;
     case OP_SWIGLU_BWD: mc = 32u; npair = 3; break;
     case OP_NT_SWIGLU:
@@ -350,6 +351,7 @@ static hipError_t run_gemm2(int op, const GemmDesc& d, int groups, hipStream_t s
     case OP_NT_ORMS: return launch_single<EPI_ORMS, 0u>(d, groups, s);
     case OP_NN_STORE: return launch_single<EPI_STORE, 2u>(d, groups, s);
     case OP_NN_RMSBWD: return launch_single<EPI_RMSBWD, 2u>(d, groups, s);
+    case OP_NT_RMSBWD: return launch_single<EPI_RMSBWD, 0u>(d, groups, s);
     case OP_NT_SWIGLU:
       switch (split_tile(d)) {
         case 3: return launch2<PBD256x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
@@ -788,6 +790,72 @@ hipError_t run_finalize(int dtype, const void* P, int64_t ldp, const float* ss, 
                        static_cast<const bf16_t*>(P), ldp, ss, rows, width, inv_D, eps,
                        static_cast<bf16_t*>(z), ldz, rms_out);
   }
+  return hipGetLastError();
+}
+
+
+// bf16 transposes: a workgroup moves one 64 x 64 tile through LDS. A
+// thread loads 16-byte chunks of two consecutive rows and writes, per
+// column, the two rows' values as one 32-bit word of the LDS tile, stored
+// column by column ([64 columns][32 row pairs + 4]); an output chunk (8
+// rows of one column) is then one 16-byte LDS read. Jobs come one after
+// another in the grid (first_tile[j] their first tile).
+struct TransposeJobs {
+  TransposeJob j[kMaxTranspose];
+  int first_tile[kMaxTranspose + 1];
+  int n;
+};
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(TransposeJobs t) {
+  __shared__ __align__(16) uint32_t tile[64][32 + 4];
+  const int b = blockIdx.x;
+  int ji = 0;
+  while (ji + 1 < t.n && b >= t.first_tile[ji + 1]) ++ji;
+  const TransposeJob& J = t.j[ji];
+  const int tcols = (J.cols + 63) / 64;
+  const int lt = b - t.first_tile[ji];
+  const int r0 = (lt / tcols) * 64, c0 = (lt % tcols) * 64;
+  const uint16_t* in = static_cast<const uint16_t*>(J.in);
+  uint16_t* out = static_cast<uint16_t*>(J.out);
+  {
+    const int p = threadIdx.x >> 3, c = (threadIdx.x & 7) * 8;  // rows 2p, 2p + 1
+    if (c0 + c < J.cols) {
+      const uint16_t* src = in + (int64_t)(r0 + 2 * p) * J.ldi + c0 + c;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(src);
+      const u32x4 bb = *reinterpret_cast<const u32x4*>(src + J.ldi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        tile[c + 2 * e][p] = (a[e] & 0xFFFFu) | (bb[e] << 16);
+        tile[c + 2 * e + 1][p] = (a[e] >> 16) | (bb[e] & 0xFFFF0000u);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int oc = (threadIdx.x >> 3) + 32 * k, ch = threadIdx.x & 7;  // rows 8 ch .. + 7
+    if (c0 + oc < J.cols) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&tile[oc][4 * ch]);
+      *reinterpret_cast<u32x4*>(out + (int64_t)(c0 + oc) * J.ldo + r0 + 8 * ch) = v;
+    }
+  }
+}
+
+hipError_t run_transpose_bf16(const TransposeJob* jobs, int n, hipStream_t s) {
+  if (n < 1 || n > kMaxTranspose) return hipErrorInvalidValue;
+  TransposeJobs t{};
+  t.n = n;
+  int tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    const TransposeJob& J = jobs[i];
+    if (J.rows % 64 != 0 || J.cols % 8 != 0 || J.rows < 0 || J.cols < 0 || !J.in || !J.out)
+      return hipErrorInvalidValue;
+    t.j[i] = J;
+    t.first_tile[i] = tiles;
+    tiles += (J.rows / 64) * ((J.cols + 63) / 64);
+  }
+  t.first_tile[n] = tiles;
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(tiles), dim3(256), 0, s, t);
   return hipGetLastError();
 }
 

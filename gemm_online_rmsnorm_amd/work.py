@@ -37,6 +37,9 @@ def kernel_work(T: int, d: int, r: int, F: int, elem: int = 2, partials: bool = 
     g("down-projection", T, r, F)
     g("down up-projection + residual", T, d, r, extra_in=e * T * d)
     # backward
+    # transposed copies of the weights the data-gradient products multiply by
+    W["transpose B_dn, A_dn, B_g, B_u, A_gu, B_o, A_o"] = (0.0, 2 * e * r * (5 * d + 3 * F))
+    W["transpose B_q, B_k, B_v, A_qkv"] = (0.0, 2 * e * 6 * r * d)
     g("dB_dn", d, r, T, out_elem=4)
     g("dd_r", T, r, d)
     if e == 2:
@@ -78,7 +81,8 @@ def kernel_work(T: int, d: int, r: int, F: int, elem: int = 2, partials: bool = 
 # "<weight gradient> split-K sum").
 MEMORY_BOUND = ("fold gamma1", "fold gamma2", "fold gamma1, gamma2", "fold gamma",
                 "QKV finalize", "gate/up finalize",
-                "row dot 1", "row dot 2", "dgamma1 column sum", "dgamma2 column sum")
+                "row dot 1", "row dot 2", "dgamma1 column sum", "dgamma2 column sum",
+                "transpose B_dn, A_dn, B_g, B_u, A_gu, B_o, A_o", "transpose B_q, B_k, B_v, A_qkv")
 
 
 def is_memory_bound(name: str) -> bool:

@@ -149,7 +149,10 @@ typedef struct {
 } lr_block_partials;
 
 /* Bytes of workspace lr_block_fwd (is_bwd = 0) or lr_block_bwd (is_bwd = 1)
- * needs for this shape; 0 if the shape is invalid. */
+ * needs for this shape; 0 if the shape is invalid. For bf16 shapes whose d,
+ * r and d_ff are multiples of 64 the backward workspace also holds
+ * transposed copies of the weights its data-gradient products multiply by
+ * (r (11 d + 3 d_ff) elements), made at the start of each stage. */
 size_t lr_block_workspace_bytes(const lr_block_shape* shape, int is_bwd);
 
 /* Where a d-wide intermediate of the checkpointed stack sits in a block
