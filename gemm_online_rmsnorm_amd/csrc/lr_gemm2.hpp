@@ -814,8 +814,15 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   static_assert(!SPLITN || FM % 2 == 0, "split tiles hand over half of the row bands");
 
   // Online RMSNorm: the waves of one row band (same wm) read the same A
-  // fragments; wave wn sums the squares of fragments i = wn, wn + NWN, ...
+  // fragments; wave wn sums the squares of bands wn, wn + NWN, ... . Its
+  // fragment slots hold the bands rotated by wn (slot i: band (i + wn) mod
+  // FM, accumulators alike), so that those bands sit in the fixed slots 0,
+  // NWN, ...: a choice by wn at run time among the slots would cost vector
+  // instructions beside every sub-step's MFMAs.
   constexpr int FSS = (FM + TL::NWN - 1) / TL::NWN;
+  constexpr bool ROT = ORMS && MCMASK == 0u && !SPLITN && !BD && FM % TL::NWN == 0 && (FM & (FM - 1)) == 0;
+  static_assert(!ORMS || (ROT && !PST), "Online RMSNorm tiles take rotated bands, one tile per workgroup");
+  auto band_of = [&](int i) { return ROT ? (i + wn) & (FM - 1) : i; };
   // ssp: this lane's part of the current panel's sums; tot: the sums of the
   // finished panels, added in panel order (lanes 0..15 hold rows 0..15 of
   // the fragment after the cross-lane sums).
@@ -826,6 +833,11 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   // of a row band only) unless the caller asked for the total.
   bool ss_panels = ORMS && g.ss_out != nullptr && !g.emit_partial && tn == 0;
   int panel = 0, in_panel = 0;
+  // The panel length is pinned in a scalar register: reloaded from the
+  // kernel arguments inside the K loop, its wait would also wait for every
+  // LDS read in flight (scalar loads and LDS reads share one counter).
+  int panel_kt = g.panel_ktiles;
+  if constexpr (ORMS) asm volatile("" : "+s"(panel_kt));
 
   // Fragment registers are double-buffered: the LDS reads of sub-step q + 1
   // (a sub-step is one 32-wide k step of one operand pair) are in flight
@@ -849,7 +861,12 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       // (slot i holds band (i + FM/2) mod FM), so that every wave keeps
       // slots 0 .. FM/2 - 1 and hands over the rest.
       const unsigned char* tAi = SPLITN ? (i < FM / 2 ? tA + srot : tA - srot) : tA;
-      if constexpr (MCMASK == 0u) {
+      if constexpr (ROT) {
+        // The swizzle repeats every 16 rows: band b is 16 rows (2 KB per
+        // 64-wide K-tile row block) further on.
+        fa[buf][i] = Opnd<BM, BK, TL::NWAVE, true>::read_frag(
+            tAi + band_of(i) * (16 * BK * 2), Opnd<BM, BK, TL::NWAVE, true>::frag_off(w0m, s, lane));
+      } else if constexpr (MCMASK == 0u) {
         fa[buf][i] = Opnd<BM, BK, TL::NWAVE, true>::read_frag(
             tAi, Opnd<BM, BK, TL::NWAVE, true>::frag_off(w0m + 16 * i, s, lane));
       } else if (amc) {
@@ -876,18 +893,22 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     if constexpr (ORMS) {
       if (p == 0) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-          if (i % TL::NWN == wn) {
+        for (int i = 0; i < FM; i += TL::NWN) {  // the slots of bands wn, wn + NWN, ...
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              // Both squares of a bf16 pair in one v_dot2c_f32_bf16 (a
-              // bf16 square is exact in fp32): a quarter of the vector
-              // instructions of unpacking and two FMAs, beside the MFMAs.
-              const bf16x8 all = __builtin_bit_cast(bf16x8, fa[buf][i]);
-              const bf16x2 v = {all[2 * c], all[2 * c + 1]};
-              ssp[i / TL::NWN] = __builtin_amdgcn_fdot2_f32_bf16(v, v, ssp[i / TL::NWN], false);
-            }
+          for (int c = 0; c < 4; ++c) {
+            // Both squares of a bf16 pair in one v_dot2c_f32_bf16 (a bf16
+            // square is exact in fp32): a quarter of the vector
+            // instructions of unpacking and two FMAs, beside the MFMAs.
+            const bf16x8 all = __builtin_bit_cast(bf16x8, fa[buf][i]);
+            const bf16x2 v = {all[2 * c], all[2 * c + 1]};
+            ssp[i / TL::NWN] = __builtin_amdgcn_fdot2_f32_bf16(v, v, ssp[i / TL::NWN], false);
           }
+        }
+        // The sums are taken in this sub-step: left alone, the compiler
+        // sinks them into the next one, whose fragment reads must then wait
+        // for them.
+#pragma unroll
+        for (int j = 0; j < FSS; ++j) asm volatile("" : "+v"(ssp[j]));
       }
     }
 #pragma unroll
@@ -995,7 +1016,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       }
     }
     if constexpr (ORMS) {
-      if (++in_panel == g.panel_ktiles || kt == nk - 1) {
+      if (++in_panel == panel_kt || kt == nk - 1) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
           if (i % TL::NWN == wn) {
@@ -1282,7 +1303,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       if constexpr (UNIFORM) {
         out.store(i, q, x);
       } else {
-        const int gr = m0 + rb + 16 * i + rr, gc = n0 + cb + 8 * cc;
+        const int gr = m0 + rb + 16 * band_of(i) + rr, gc = n0 + cb + 8 * cc;
         if (gr < M && gc < N)
           __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(static_cast<bf16_t*>(cbase) +
                                                                  (int64_t)gr * ldc + gc));
@@ -1340,7 +1361,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
         }
       }
       float rs = 1.0f;  // 1 / rms_g, 1 / rowdiv, or the RMSNorm-backward coefficient
-      if constexpr (ORMS) rs = sRow[rb + 16 * i + fr];
+      if constexpr (ORMS) rs = sRow[rb + 16 * band_of(i) + fr];
       if constexpr (EPI == EPI_STORE) rs = 1.0f / rowv[i];
       if constexpr (EPI == EPI_RMSBWD) rs = rowv[i];
       u32x2 pk[NOUT][FN];  // this band's packed bf16 outputs
