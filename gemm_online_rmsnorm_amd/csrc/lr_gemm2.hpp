@@ -89,6 +89,16 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 // The compiler schedules no instruction across this point.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N - 1>{}).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
 // A value that is the same in every lane of a wave, moved to a scalar register.
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -408,27 +418,52 @@ struct Opnd {
     }
   }
 
+  // IMM: a constant byte offset, an immediate of the transposing reads.
+  template <int IMM = 0>
   __device__ static __forceinline__ u32x4 read_frag(const unsigned char* tile, int off) {
-    if constexpr (KC) {
-      return *reinterpret_cast<const u32x4*>(tile + off);
-    } else {
-      // The second read is 4 k-rows further down; its swizzle is the same
-      // (k & 3 and (k >> 3) & 1 do not change when k grows by 4 within a
-      // lane's 8-row group). The reads are issued as inline assembly: the
-      // compiler would otherwise make each wait for every pending
-      // HBM-to-LDS load, which serialises the pipeline. The caller waits
-      // for them (wait_lgkmcnt0) before the fragments are used.
-      const uint32_t a = lds_addr(tile + off);
-      bf16x4 lo, hi;
-      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a));
-      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(a), "n"(4 * R * 2));
-      u32x4 r;
-      r[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
-      r[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3));
-      r[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1));
-      r[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3));
-      return r;
-    }
+    if constexpr (KC)
+      return *reinterpret_cast<const u32x4*>(tile + off + IMM);
+    else
+      return read_tr<IMM>(lds_addr(tile + off));
+  }
+  // The two transposing reads of an M-contiguous fragment at LDS address a.
+  // The second read is 4 k-rows further down; its swizzle is the same (k & 3
+  // and (k >> 3) & 1 do not change when k grows by 4 within a lane's 8-row
+  // group). The reads are issued as inline assembly: the compiler would
+  // otherwise make each wait for every pending HBM-to-LDS load, which
+  // serialises the pipeline. The caller waits for them (wait_lgkmcnt0)
+  // before the fragments are used.
+  template <int IMM>
+  __device__ static __forceinline__ u32x4 read_tr(uint32_t a) {
+    static_assert(!KC, "transposing reads are for M-contiguous tiles");
+    static_assert(IMM >= 0 && IMM + 4 * R * 2 < 65536, "LDS instruction offsets are 16-bit");
+    bf16x4 lo, hi;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(a), "n"(IMM));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(a), "n"(IMM + 4 * R * 2));
+    u32x4 r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3));
+    return r;
+  }
+
+  // Fragment of rows w0 .. w0 + 15 at the 32-wide k-step ST of the tile.
+  // An M-contiguous fragment one k-step on lies 32 k-rows further down with
+  // the same swizzle (k & 3 and (k >> 3) & 1 do not change by 32): the step
+  // is an immediate of the read instruction, not an address computation.
+  template <int ST>
+  __device__ static __forceinline__ u32x4 read_step(const unsigned char* tile, int w0, int lane) {
+    if constexpr (KC)
+      return read_frag(tile, frag_off(w0, ST, lane));
+    else
+      return read_tr<ST * 32 * R * 2>(lds_addr(tile) + frag_off(w0, 0, lane));
+  }
+  // The same for an M-contiguous tile at LDS address base (the same in every
+  // lane, in a scalar register): one vector add per fragment.
+  template <int ST>
+  __device__ static __forceinline__ u32x4 read_step_at(uint32_t base, int w0, int lane) {
+    return read_tr<ST * 32 * R * 2>(base + frag_off(w0, 0, lane));
   }
 };
 
@@ -847,14 +882,21 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   constexpr int Q = ((SPLITN || BD) ? 1 : NPAIR) * TL::NSTEP;
   u32x4 fa[2][FM], fb[2][FN];
   // st: the stage of K-tile kt (one ring); separate rings use kt.
-  auto read_q = [&](int kt, const unsigned char* st, int q, int buf) {
-    const int p = q / TL::NSTEP, s = q % TL::NSTEP;
+  auto read_q = [&](int kt, const unsigned char* st, auto q_tag, int buf) {
+    constexpr int q = decltype(q_tag)::value;
+    constexpr int p = q / TL::NSTEP, s = q % TL::NSTEP;
     const unsigned char* tA = TL::ASYM ? a_stage(kt)
                               : SPLITN ? st + pw * BM * BK * 2 : st + p * (BM + BN) * BK * 2;
     const unsigned char* tB = TL::ASYM ? b_stage(kt)
                               : SPLITN ? st + 2 * BM * BK * 2 : tA + BM * BK * 2;
     const bool amc = (MCMASK >> (2 * p)) & 1u;
     const bool bmc = (MCMASK >> (2 * p + 1)) & 1u;
+    // The tiles' LDS addresses as one scalar each: left to itself the
+    // compiler splits the ring offset into parts and spends two vector
+    // instructions per transposing fragment read on them.
+    uint32_t ta = lds_addr(tA), tb = lds_addr(tB);
+    if constexpr ((MCMASK & 0x15u) != 0u && !SPLITN) asm volatile("" : "+s"(ta));
+    if constexpr ((MCMASK & 0x2Au) != 0u) asm volatile("" : "+s"(tb));
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       // Split tiles: the up-pair waves hold row bands in rotated order
@@ -867,24 +909,20 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
         fa[buf][i] = Opnd<BM, BK, TL::NWAVE, true>::read_frag(
             tAi + band_of(i) * (16 * BK * 2), Opnd<BM, BK, TL::NWAVE, true>::frag_off(w0m, s, lane));
       } else if constexpr (MCMASK == 0u) {
-        fa[buf][i] = Opnd<BM, BK, TL::NWAVE, true>::read_frag(
-            tAi, Opnd<BM, BK, TL::NWAVE, true>::frag_off(w0m + 16 * i, s, lane));
+        fa[buf][i] = Opnd<BM, BK, TL::NWAVE, true>::template read_step<s>(tAi, w0m + 16 * i, lane);
       } else if (amc) {
-        fa[buf][i] = Opnd<BM, BK, TL::NWAVE, false>::read_frag(
-            tAi, Opnd<BM, BK, TL::NWAVE, false>::frag_off(w0m + 16 * i, s, lane));
+        fa[buf][i] = SPLITN ? Opnd<BM, BK, TL::NWAVE, false>::template read_step<s>(tAi, w0m + 16 * i, lane)
+                            : Opnd<BM, BK, TL::NWAVE, false>::template read_step_at<s>(ta, w0m + 16 * i, lane);
       } else {
-        fa[buf][i] = Opnd<BM, BK, TL::NWAVE, true>::read_frag(
-            tAi, Opnd<BM, BK, TL::NWAVE, true>::frag_off(w0m + 16 * i, s, lane));
+        fa[buf][i] = Opnd<BM, BK, TL::NWAVE, true>::template read_step<s>(tAi, w0m + 16 * i, lane);
       }
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       if (bmc)
-        fb[buf][j] = Opnd<BN, BK, TL::NWAVE, false>::read_frag(
-            tB, Opnd<BN, BK, TL::NWAVE, false>::frag_off(w0n + 16 * j, s, lane));
+        fb[buf][j] = Opnd<BN, BK, TL::NWAVE, false>::template read_step_at<s>(tb, w0n + 16 * j, lane);
       else
-        fb[buf][j] = Opnd<BN, BK, TL::NWAVE, true>::read_frag(
-            tB, Opnd<BN, BK, TL::NWAVE, true>::frag_off(w0n + 16 * j, s, lane));
+        fb[buf][j] = Opnd<BN, BK, TL::NWAVE, true>::template read_step<s>(tB, w0n + 16 * j, lane);
     }
   };
   // ph: the pair a block-diagonal tile's current K-tile belongs to.
@@ -967,7 +1005,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   pro_post(std::integral_constant<int, 0>{});
 
   for (;;) {  // the tiles of a persistent workgroup (one otherwise)
-  read_q(0, stage_ptr(0), 0, 0);
+  read_q(0, stage_ptr(0), std::integral_constant<int, 0>{}, 0);
   // Fragment reads are in flight only inside the loop body, between a
   // sub-step's start and the next sub-step's wait: every path into and out
   // of the loop has them landed, so code the compiler places at the loop's
@@ -982,8 +1020,8 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   auto ktile = [&](int kt, auto b0_tag, auto ph_tag) {
     constexpr int B0 = decltype(b0_tag)::value;
     const unsigned char* st = stage_ptr(kt % S);
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
+    static_for<Q>([&](auto q_tag) {
+      constexpr int q = decltype(q_tag)::value;
       const int buf = (q + B0) & 1;
       // Nothing is scheduled across this wait in either direction: the
       // fragments of sub-step q (some read by inline assembly the compiler
@@ -991,8 +1029,8 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       sched_fence();
       wait_lgkmcnt0();
       sched_fence();
-      if (q + 1 < Q) {
-        read_q(kt, st, q + 1, buf ^ 1);
+      if constexpr (q + 1 < Q) {
+        read_q(kt, st, std::integral_constant<int, q + 1>{}, buf ^ 1);
         compute_q(q, buf, ph_tag);
         interleave<NDS, 0, FM * FN>();
       } else {
@@ -1010,11 +1048,11 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
           block_barrier();
           issue(kt + S);
         }
-        read_q(kt + 1, stage_ptr((kt + 1) % S), 0, buf ^ 1);
+        read_q(kt + 1, stage_ptr((kt + 1) % S), std::integral_constant<int, 0>{}, buf ^ 1);
         compute_q(q, buf, ph_tag);
         interleave<NDS, L, FM * FN>();
       }
-    }
+    });
     if constexpr (ORMS) {
       if (++in_panel == panel_kt || kt == nk - 1) {
 #pragma unroll
