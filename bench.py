@@ -201,16 +201,17 @@ def _calibration_copy(torch):
     torch.cuda.synchronize()
 
 
-def _traffic_record(bench_name):
+def _traffic_record(bench_name, workload):
     """Measured HBM bytes per launch of the named launch, from the record in
-    profiles/ taken on the current kernel sources; None without one."""
+    profiles/ taken on the current kernel sources and on this workload; None
+    without one."""
     from gemm_online_rmsnorm_amd import traffic as lrtraffic
     if not os.path.isdir(TRAFFIC_DIR):
         return None
     for name in sorted(os.listdir(TRAFFIC_DIR)):
         if name.startswith("traffic_") and name.endswith(".json"):
             rec = lrtraffic.load(os.path.join(TRAFFIC_DIR, name))
-            if rec and rec.get("bench_name") == bench_name:
+            if rec and rec.get("bench_name") == bench_name and rec.get("workload") == workload:
                 return rec["traffic_bytes"]
     return None
 
@@ -491,7 +492,7 @@ def attention_main(args):
     attn_bytes = {"attention fwd": qb + 2 * kb + qb + rowb,
                   "attention bwd dQ": 3 * qb + 2 * kb + rowb + qb + 2 * rowb,
                   "attention bwd dK dV": 2 * qb + 2 * kb + 2 * rowb + 2 * kb}
-    traffic, traffic_alg = _traffic_record(dom["kernel"]), None
+    traffic, traffic_alg = _traffic_record(dom["kernel"], s.name), None
     if traffic is not None:
         traffic_alg = attn_bytes[dom["kernel"]]
     flop = 14 * s.dh * pairs * s.H
@@ -611,18 +612,20 @@ def main():
         run.step(stream)
     torch.cuda.synchronize()
     lr.profile_enable(False)
-    prof = lr.profile_collect()
+    prof = lr.profile_collect(with_bytes=True)
     elem = 2 if s.dtype == "bf16" else 4
     work = kernel_work(s.T, s.d, s.r, s.F, elem, s.partials, s.P)
     kernels = []
-    for name, count, total in prof:
+    for name, count, total, nbytes in prof:
         per = total / count
-        fl, by = work.get(name, (0.0, 0.0))
+        # Launches whose bytes depend on a choice made at run time (the
+        # split-K sums) take the count the library recorded for them.
+        fl, by = work.get(name, (0.0, nbytes / count if count else 0.0))
         kernels.append({
             "kernel": name, "launches_per_step": count // args.steps,
             "ms": round(per, 4),
             "tflops": round(fl / (per * 1e-3) / 1e12, 1) if fl else None,
-            "gbs": round(by / (per * 1e-3) / 1e9, 1),
+            "gbs": round(by / (per * 1e-3) / 1e9, 1) if by else None,
             "bound": "hbm" if is_memory_bound(name) else "mfma",
             "step_ms": round(total / args.steps, 4),
         })
@@ -659,7 +662,7 @@ def main():
     }
     # Measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE,
     # copy-calibrated), when taken on the current kernel sources.
-    roofline["traffic"] = _traffic_record(dom["kernel"])
+    roofline["traffic"] = _traffic_record(dom["kernel"], s.name)
     if roofline["traffic"] is not None:
         roofline["traffic_algorithmic_bytes"] = round(work[dom["kernel"]][1])
     roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)

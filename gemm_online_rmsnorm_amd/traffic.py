@@ -11,10 +11,11 @@ byte count over what the counter read for it.
     rocprofv3 --pmc WRITE_SIZE -d D2 -o w -f csv -- python bench.py --copy-calibration ...
     python -m gemm_online_rmsnorm_amd.traffic D1/.../f_counter_collection.csv \\
         D2/.../w_counter_collection.csv --bench-name "SwiGLU recompute + backward" \\
-        --kernel "gemm2_kernel<...>" --copy-bytes N -o profiles/<name>.json
+        --kernel "gemm2_kernel<...>" --workload 7B-bf16 --copy-bytes N -o profiles/<name>.json
 
-The result carries a hash of the kernel sources; bench.py reports it only
-while the sources are unchanged.
+The result carries a hash of the kernel sources and the name of the workload
+it was measured on; bench.py reports it only for that workload and while the
+sources are unchanged.
 """
 from __future__ import annotations
 
@@ -111,6 +112,8 @@ def main() -> None:
     ap.add_argument("--kernel", required=True, help="substring of the kernel's name")
     ap.add_argument("--bench-name", required=True, help="the launch's name in bench.py")
     ap.add_argument("--copy-bytes", type=int, required=True)
+    ap.add_argument("--workload", required=True,
+                    help="the profiled workload's name (bench.py reports the record for it only)")
     ap.add_argument("--command", default="", help="the profiled command, for the record")
     ap.add_argument("--attention", action="store_true",
                     help="an attention kernel: hash the attention sources")
@@ -119,6 +122,7 @@ def main() -> None:
     rec = measure(a.fetch_csv, a.write_csv, a.kernel, a.copy_bytes,
                   ATTENTION_SOURCES if a.attention else KERNEL_SOURCES)
     rec["bench_name"] = a.bench_name
+    rec["workload"] = a.workload
     rec["command"] = a.command
     with open(a.out, "w") as f:
         json.dump(rec, f, indent=1)

@@ -76,3 +76,20 @@ def test_record_follows_its_own_sources(tmp_path):
     assert traffic.load(str(path)) == rec
     path.write_text(json.dumps(rec | {"source_sha256": "0" * 64}))
     assert traffic.load(str(path)) is None
+
+
+def test_bench_reports_a_record_for_its_own_workload_only(tmp_path, monkeypatch):
+    """bench.py takes a record for the launch it names and the workload it was
+    measured on; the same launch of another workload reports none."""
+    import json
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    rec = {"source_sha256": traffic.source_hash(), "sources": list(traffic.KERNEL_SOURCES),
+           "traffic_bytes": 123, "bench_name": "SwiGLU recompute + backward", "workload": "7B-bf16"}
+    (tmp_path / "traffic_x.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "TRAFFIC_DIR", str(tmp_path))
+    assert bench._traffic_record("SwiGLU recompute + backward", "7B-bf16") == 123
+    assert bench._traffic_record("SwiGLU recompute + backward", "1B-bf16") is None
+    assert bench._traffic_record("dgu_r", "7B-bf16") is None
