@@ -44,6 +44,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #define LR_GPTR(p) ((__attribute__((address_space(1))) void*)(p))
 #define LR_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
+#ifndef LR_SPLIT_AB
+#define LR_SPLIT_AB 1
+#endif
 
 // NSPLIT = 2: a two-pair tile whose B rows hold pair 0's BN / 2 rows, then
 // pair 1's; waves of the first NWN / 2 columns multiply pair 0, the others
@@ -697,6 +700,18 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   // through three stages, are faster with the older half issuing (measured:
   // all eight waves issuing made the SwiGLU tiles 3-5% slower).
   constexpr int NDMA = (TL::NWAVE == 8 && MCMASK == 0u && !SPLITN) ? TL::NWAVE / 2 : TL::NWAVE;
+  // Separate rings with half the waves loading: the older half loads the B
+  // tiles (after the barrier of K-tile k, B of k + 2) and the younger half
+  // the A tiles (at the start of K-tile k, A of k + 2, into the stage K-tile
+  // k - 1 freed). A wave stalls while its loads enter the load path; split
+  // so, each wave has half the loads, and the two waves of a SIMD stall at
+  // different points of the K-tile, each while the other issues MFMAs.
+  // (Not the Online RMSNorm tile: at 256 VGPRs already, it spilled so.)
+  constexpr bool SPLIT_AB = LR_SPLIT_AB && TL::ASYM && 2 * NDMA == TL::NWAVE && !ORMS;
+  // A loader's wave index among the waves that issue its loads.
+  const int dwave = SPLIT_AB ? wave % NDMA : wave;
+  const bool a_iss = SPLIT_AB ? wave >= NDMA : (NDMA == TL::NWAVE || wave < NDMA);
+  const bool b_iss = SPLIT_AB ? wave < NDMA : (NDMA == TL::NWAVE || wave < NDMA);
   using OA0 = Opnd<BM, BK, NDMA, !(MCMASK & 1u)>;
   using OB0 = Opnd<BNO, BK, NDMA, !(MCMASK & 2u)>;
   using OA1 = Opnd<BM, BK, NDMA, !(MCMASK & 4u)>;
@@ -722,8 +737,8 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     pa[0] = static_cast<const bf16_t*>(pick3(g.a, p0));
     pb[0] = static_cast<const bf16_t*>(pick3(g.b, p0));
     const int64_t lda0 = pick3(g.lda, p0), ldb0 = pick3(g.ldb, p0);
-    a0.init(lda0, m0_, M_, lane, wave);
-    b0.init(ldb0, n0_, N_, lane, wave);
+    a0.init(lda0, m0_, M_, lane, dwave);
+    b0.init(ldb0, n0_, N_, lane, dwave);
     ea[0] = OA0::extent(lda0, M_, g.K);
     eb[0] = OB0::extent(ldb0, N_, g.K);
     sa[0] = (MCMASK & 1u) ? (int64_t)BK * lda0 : BK;
@@ -772,14 +787,14 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
   // Separate rings: one operand's loads of K-tile kt (the same empty range
   // past the last K-tile as below).
   auto issue_a = [&](int kt) {
-    if (NDMA < TL::NWAVE && wave >= NDMA) return;
+    if (!a_iss) return;
     const uint32_t n = kt < g.ktiles_split ? (uint32_t)(2 * (ea[0] - kt * sa[0])) : 0u;
-    a0.issue(pa[0] + kt * sa[0], n, a_stage(kt), wave);
+    a0.issue(pa[0] + kt * sa[0], n, a_stage(kt), dwave);
   };
   auto issue_b = [&](int kt) {
-    if (NDMA < TL::NWAVE && wave >= NDMA) return;
+    if (!b_iss) return;
     const uint32_t n = kt < g.ktiles_split ? (uint32_t)(2 * (eb[0] - kt * sb[0])) : 0u;
-    b0.issue(pb[0] + kt * sb[0], n, b_stage(kt), wave);
+    b0.issue(pb[0] + kt * sb[0], n, b_stage(kt), dwave);
   };
   auto issue = [&](int kt) {
     if (NDMA < TL::NWAVE && wave >= NDMA) return;
@@ -990,13 +1005,23 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     }
   };
   auto pro_post = [&](auto after_tag) {
-    constexpr int W = (TL::ASYM ? LA : VM_AFTER) + decltype(after_tag)::value;
-    wait_vmcnt<(W < 63 ? W : 63)>();
+    constexpr int AF = decltype(after_tag)::value;
+    constexpr int W = (TL::ASYM ? LA : VM_AFTER) + AF;
+    if constexpr (SPLIT_AB) {
+      // B loaders: B of K-tile 0 has landed with at most AF operations
+      // pending; A loaders: A of K-tile 0 with at most LA + AF (A of 1).
+      if (b_iss)
+        wait_vmcnt<(AF < 63 ? AF : 63)>();
+      else
+        wait_vmcnt<(W < 63 ? W : 63)>();
+    } else {
+      wait_vmcnt<(W < 63 ? W : 63)>();
+    }
     wait_lgkmcnt0();  // every wave's epilogue is done with its LDS areas
     block_barrier();
     if constexpr (TL::ASYM) {
       issue_b(1);
-      issue_a(2);
+      if constexpr (!SPLIT_AB) issue_a(2);  // (split: at the start of K-tile 0)
     } else {
       issue(S - 1);
     }
@@ -1029,6 +1054,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       sched_fence();
       wait_lgkmcnt0();
       sched_fence();
+      if constexpr (SPLIT_AB && q == 0) issue_a(kt + 2);
       if constexpr (q + 1 < Q) {
         read_q(kt, st, std::integral_constant<int, q + 1>{}, buf ^ 1);
         compute_q(q, buf, ph_tag);
@@ -1038,7 +1064,16 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
         // passes the barrier; the stage of K-tile kt is then free for
         // K-tile kt + S, and K-tile kt + 1 has landed. (On the last K-tile
         // this reads a stage no MFMA uses.)
-        if constexpr (TL::ASYM) {
+        if constexpr (SPLIT_AB) {
+          // B loaders: B of K-tile kt + 1 (issued one K-tile ago) is their
+          // only load in flight; A loaders: A of kt + 1 and of kt + 2.
+          if (b_iss)
+            wait_vmcnt<0>();
+          else
+            wait_vmcnt<LA>();
+          block_barrier();
+          issue_b(kt + 2);
+        } else if constexpr (TL::ASYM) {
           wait_vmcnt<LA>();
           block_barrier();
           issue_b(kt + 2);
