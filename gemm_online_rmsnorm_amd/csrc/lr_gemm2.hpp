@@ -63,6 +63,10 @@ struct Tile2 {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, NWM = NWM_, NWN = NWN_;
   static constexpr int NSTAGE = NSTAGE_;
   static constexpr bool BDIAG = BDIAG_ != 0;
+  // BDIAG_ = 2: the first pair's results (the gate) are packed to bf16 once
+  // its K loop is done, and the second pair accumulates in the same
+  // registers: half the accumulator registers of BDIAG_ = 1 for the gate.
+  static constexpr bool BDPACK = BDIAG_ == 2;
   // NSTAGE_A_ > 0: the A operand (the streamed activation of a one-pair
   // product) gets a ring of its own with NSTAGE_A_ stages and B keeps
   // NSTAGE, so A's loads are issued NSTAGE_A_ - 1 K-tiles ahead.
@@ -611,8 +615,14 @@ constexpr int gemm2_lds_bytes() {
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
+// The 4-wave packed block-diagonal tile runs two workgroups per CU, so its
+// registers are held to two waves per SIMD (256).
+template <class TL>
+constexpr int gemm2_min_waves() {
+  return (TL::BDPACK && TL::NWAVE == 4) ? 2 : 1;
+}
 template <class TL, int NPAIR, uint32_t MCMASK, int EPI>
-__global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
+__global__ __launch_bounds__(TL::NT, gemm2_min_waves<TL>()) void gemm2_kernel(GemmArgs g) {
   constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, S = TL::NSTAGE;
   constexpr int FM = TL::FM, FN = TL::FN;
   constexpr bool ORMS = (EPI == EPI_ORMS);
@@ -846,8 +856,11 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
                 "both pairs of a block-diagonal tile load alike");
   static_assert(L * (S - 1) < 64, "too many loads in flight for vmcnt");
 
-  constexpr int NACC = SPLITN ? 1 : NPAIR;
+  constexpr bool BDP = TL::BDPACK;
+  static_assert(!BDP || BD, "packing is for block-diagonal tiles");
+  constexpr int NACC = (SPLITN || BDP) ? 1 : NPAIR;
   f32x4 acc[NACC][FM][FN];
+  u32x2 gpk[BDP ? FM : 1][BDP ? FN : 1];  // the first pair's results, bf16
 #pragma unroll
   for (int p = 0; p < NACC; ++p)
 #pragma unroll
@@ -921,23 +934,23 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       if constexpr (ROT) {
         // The swizzle repeats every 16 rows: band b is 16 rows (2 KB per
         // 64-wide K-tile row block) further on.
-        fa[buf][i] = Opnd<BM, BK, TL::NWAVE, true>::read_frag(
-            tAi + band_of(i) * (16 * BK * 2), Opnd<BM, BK, TL::NWAVE, true>::frag_off(w0m, s, lane));
+        fa[buf][i] = Opnd<BM, BK, NDMA, true>::read_frag(
+            tAi + band_of(i) * (16 * BK * 2), Opnd<BM, BK, NDMA, true>::frag_off(w0m, s, lane));
       } else if constexpr (MCMASK == 0u) {
-        fa[buf][i] = Opnd<BM, BK, TL::NWAVE, true>::template read_step<s>(tAi, w0m + 16 * i, lane);
+        fa[buf][i] = Opnd<BM, BK, NDMA, true>::template read_step<s>(tAi, w0m + 16 * i, lane);
       } else if (amc) {
-        fa[buf][i] = SPLITN ? Opnd<BM, BK, TL::NWAVE, false>::template read_step<s>(tAi, w0m + 16 * i, lane)
-                            : Opnd<BM, BK, TL::NWAVE, false>::template read_step_at<s>(ta, w0m + 16 * i, lane);
+        fa[buf][i] = SPLITN ? Opnd<BM, BK, NDMA, false>::template read_step<s>(tAi, w0m + 16 * i, lane)
+                            : Opnd<BM, BK, NDMA, false>::template read_step_at<s>(ta, w0m + 16 * i, lane);
       } else {
-        fa[buf][i] = Opnd<BM, BK, TL::NWAVE, true>::template read_step<s>(tAi, w0m + 16 * i, lane);
+        fa[buf][i] = Opnd<BM, BK, NDMA, true>::template read_step<s>(tAi, w0m + 16 * i, lane);
       }
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       if (bmc)
-        fb[buf][j] = Opnd<BN, BK, TL::NWAVE, false>::template read_step_at<s>(tb, w0n + 16 * j, lane);
+        fb[buf][j] = Opnd<BN, BK, NDMA, false>::template read_step_at<s>(tb, w0n + 16 * j, lane);
       else
-        fb[buf][j] = Opnd<BN, BK, TL::NWAVE, true>::template read_step<s>(tB, w0n + 16 * j, lane);
+        fb[buf][j] = Opnd<BN, BK, NDMA, true>::template read_step<s>(tB, w0n + 16 * j, lane);
     }
   };
   // ph: the pair a block-diagonal tile's current K-tile belongs to.
@@ -967,7 +980,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) mfma_step<bf16_t>(fb[buf][j], fa[buf][i], acc[p][i][j]);
+      for (int j = 0; j < FN; ++j) mfma_step<bf16_t>(fb[buf][j], fa[buf][i], acc[BDP ? 0 : p][i][j]);
   };
   // K-tile kt has landed in LDS when at most (K-tiles issued after it) x L
   // loads of this lane remain; `after` is that count of K-tiles.
@@ -1118,6 +1131,18 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     // nk K-tiles of pair 0, then nk of pair 1 (nk = ktiles_split each).
     static_assert(!(Q & 1), "block-diagonal tiles take an even sub-step count");
     for (int kt = 0; kt < nk; ++kt) ktile(kt, I0{}, I0{});
+    if constexpr (BDP) {
+      // The gate is final: keep it as bf16 (half the registers) and clear
+      // the accumulators for the up pair.
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          gpk[i][j] = u32x2{pack_bf16x2(acc[0][i][j][0], acc[0][i][j][1]),
+                            pack_bf16x2(acc[0][i][j][2], acc[0][i][j][3])};
+          acc[0][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
     for (int kt = nk; kt < 2 * nk; ++kt) ktile(kt, I0{}, I1{});
   } else if constexpr (Q & 1) {
     for (int kt = 0; kt < nk; kt += 2) {
@@ -1312,6 +1337,18 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
     }
   }
 #define LR_E(p, i, j) acc[SPLITN ? 0 : (p)][SPLITN ? (p) * FME + (i) : (i)][j]
+  // The gate value g of element v of band i, fragment j, as it enters the
+  // SiLU: a bf16 value in every tile (the packed gate, or the accumulator
+  // rounded to bf16, as a bf16 GEMM would store it), so that the forward
+  // and the recompute in the backward agree bitwise whichever tiles they run.
+  auto gate_of = [&](int i, int j, int v) -> float {
+    if constexpr (BDP) {
+      const uint32_t w = gpk[i][j][v >> 1];
+      return (v & 1) ? bf16_hi(w) : bf16_lo(w);
+    } else {
+      return bf16_lo(pack_bf16x2(LR_E(0, i, j)[v], 0.f));
+    }
+  };
 
   // Elementwise combination of the accumulators.
   if constexpr (EPI == EPI_SWIGLU) {
@@ -1321,8 +1358,11 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float gg = LR_E(0, i, j)[v];
-          LR_E(0, i, j)[v] = gg * sigmoid_f<bf16_t>(gg) * LR_E(1, i, j)[v];
+          const float gg = gate_of(i, j, v);
+          if constexpr (BDP)  // the up values in the accumulators
+            acc[0][i][j][v] = gg * sigmoid_f<bf16_t>(gg) * acc[0][i][j][v];
+          else
+            LR_E(0, i, j)[v] = gg * sigmoid_f<bf16_t>(gg) * LR_E(1, i, j)[v];
         }
   }
   if constexpr (EPI == EPI_SWIGLU_BWD) {
@@ -1446,7 +1486,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
         if constexpr (IN && HAS_H) unpack4(hin[j], hv);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float x = LR_E(0, i, j)[v];
+          const float x = (EPI == EPI_SWIGLU_BWD2) ? gate_of(i, j, v) : LR_E(0, i, j)[v];
           if constexpr (EPI == EPI_STORE) {
             o[0][v] = (g.rowdiv ? x * rs : x) + rv[v];
           } else if constexpr (EPI == EPI_ORMS) {
@@ -1466,7 +1506,7 @@ __global__ __launch_bounds__(TL::NT) void gemm2_kernel(GemmArgs g) {
             // m = SiLU(g) u; dg = dm u sig(g)(1 + g(1 - sig(g))); du = dm SiLU(g)
             // (SiLU'(g) = sig(g) + SiLU(g) (1 - sig(g)): one FMA on values
             // already at hand; the epilogue is bound by its vector work.)
-            const float uu = LR_E(1, i, j)[v], dm = rv[v];
+            const float uu = LR_E(BDP ? 0 : 1, i, j)[v], dm = rv[v];  // (packed: up in acc[0])
             const float sg = sigmoid_f<bf16_t>(x);
             const float sl = x * sg;
             const float ds = __builtin_fmaf(sl, 1.0f - sg, sg);

@@ -135,14 +135,16 @@ using PS192x128 = Tile2<192, 256, 64, 2, 4, 2, 2>;
 // A and B tiles (48 KB), so three stages fit, and every wave (64 x 64 of
 // both) combines g and u in registers without an exchange.
 using PBD256x128 = Tile2<256, 128, 64, 4, 2, 3, 1, 0, 1>;
-// The block-diagonal tile at 128 x 128 with 4 waves and two 32 KB stages:
-// two workgroups share a CU and drift apart, so one tile's epilogue runs
-// beside the other's main loop. The SwiGLU recompute + backward, whose
-// epilogue (SiLU, its derivative, three outputs) is bound by vector work,
-// runs it (measured: 949 -> 903 us at the 7B shape, the step 0.3% faster
-// net of the kernels after it); the forward, with a quarter of that
-// epilogue work, is 3% faster on the 256 x 128 tile.
-using PBD128x128 = Tile2<128, 128, 64, 2, 2, 2, 1, 0, 1>;
+// The block-diagonal tile at 160 x 128 with 4 waves of 80 x 64 and two 36
+// KB stages, the gate packed to bf16 once the gate pair is done (which
+// frees the registers for 80-row wave tiles at two waves per SIMD): two
+// workgroups share a CU and drift apart, so one tile's epilogue runs beside
+// the other's main loop. Both SwiGLU products run it; against the 256 x
+// 128 tile (forward) and a 128 x 128 tile with fp32 gate accumulators
+// (recompute + backward) it moves 10% fewer bytes per FLOP from L2 and
+// through LDS (measured at the 7B shape: forward 722 -> 679 us, recompute
+// + backward 882 -> 794 us, the step 1% faster).
+using PBDP160x128 = Tile2<160, 128, 64, 2, 2, 2, 1, 0, 2>;
 
 // Compute units of the current device (looked up once per device).
 static int device_cus() {
@@ -302,13 +304,12 @@ static hipError_t launch_single(const GemmDesc& d, int groups, hipStream_t s) {
   }
 }
 
-// Tile choice of the gate/up pair GEMMs: 4 the block-diagonal 128 x 128
-// tile, two per CU (the recompute + backward), 3 the block-diagonal 256 x
-// 128 tile, 0 the 192-row split tile (k-tiles of 64), 1 the 256-row split
-// tile (k-tiles of 32), 2 the 128 x 128 two-pair tile for grids that would
-// leave CUs idle.
-static int split_tile(const GemmDesc& d, bool bwd = false) {
-  if (bwd && d.K % 64 == 0 && ntiles(d, 128, 128, 1) >= 2 * kCUs) return 4;
+// Tile choice of the gate/up pair GEMMs: 4 the packed block-diagonal 160 x
+// 128 tile, two per CU, 3 the block-diagonal 256 x 128 tile, 0 the 192-row
+// split tile (k-tiles of 64), 1 the 256-row split tile (k-tiles of 32), 2
+// the 128 x 128 two-pair tile for grids that would leave CUs idle.
+static int split_tile(const GemmDesc& d) {
+  if (d.K % 64 == 0 && ntiles(d, 160, 128, 1) >= 2 * kCUs) return 4;
   if (d.K % 64 == 0 && ntiles(d, 256, 128, 1) >= kCUs) return 3;
   if (d.K % 64 == 0 && ntiles(d, 192, 128, 1) >= kCUs) return 0;
   if (ntiles(d, 256, 128, 1) >= kCUs) return 1;
@@ -354,6 +355,7 @@ static hipError_t run_gemm2(int op, const GemmDesc& d, int groups, hipStream_t s
     case OP_NT_RMSBWD: return launch_single<EPI_RMSBWD, 0u>(d, groups, s);
     case OP_NT_SWIGLU:
       switch (split_tile(d)) {
+        case 4: return launch2<PBDP160x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
         case 3: return launch2<PBD256x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
         case 0: return launch2<PS192x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
         case 1: return launch2<PS256x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
@@ -361,8 +363,8 @@ static hipError_t run_gemm2(int op, const GemmDesc& d, int groups, hipStream_t s
       }
     case OP_SWIGLU_BWD: return launch2<P3x128x128, 3, 32u, EPI_SWIGLU_BWD>(d, 1, s);
     case OP_SWIGLU_BWD2:
-      switch (split_tile(d, true)) {
-        case 4: return launch2<PBD128x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
+      switch (split_tile(d)) {
+        case 4: return launch2<PBDP160x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
         case 3: return launch2<PBD256x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
         case 0: return launch2<PS192x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
         case 1: return launch2<PS256x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
@@ -378,8 +380,8 @@ static int engine2_bk(int op) {
 
 int gemm2_tile_m(int op, const GemmDesc& d, int groups) {
   if (op == OP_NT_SWIGLU || op == OP_SWIGLU_BWD2) {
-    const int t = split_tile(d, op == OP_SWIGLU_BWD2);
-    return t == 0 ? 192 : ((t == 1 || t == 3) ? 256 : 128);
+    const int t = split_tile(d);
+    return t == 4 ? 160 : t == 0 ? 192 : ((t == 1 || t == 3) ? 256 : 128);
   }
   if (op == OP_SWIGLU_BWD) return 128;
   return single_tile(d, groups) == 2 ? 128 : 256;
