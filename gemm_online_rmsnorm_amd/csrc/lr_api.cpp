@@ -1033,8 +1033,12 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       g.c[2] = W.du;
       g.ldc[2] = F;
       // On the pipelined engine dm = dd_r A_dn is its own GEMM (written into
-      // du's buffer), then one two-pair tile recomputes g and u and reads dm
-      // in its epilogue, which overwrites dm with du element by element.
+      // du's buffer, on whichever engine takes its shape), then one two-pair
+      // tile recomputes g and u and reads dm in its epilogue, which
+      // overwrites dm with du element by element. The two-pair tile takes
+      // exactly the shapes the forward's gate/up tile takes, so the gate is
+      // rounded alike in both (bitwise equal m); other shapes run both on the
+      // general engine.
       lr::GemmDesc dmg;
       dmg.M = T;
       dmg.N = F;
@@ -1050,8 +1054,7 @@ int lr_block_bwd(const lr_block_shape* s, const lr_block_weights* w, const void*
       two.b[2] = nullptr;
       two.res = W.du;
       two.ldres = F;
-      if (lr::uses_engine2(lr::OP_NN_STORE, dt, dmg, 1) &&
-          lr::uses_engine2(lr::OP_SWIGLU_BWD2, dt, two, 1)) {
+      if (lr::uses_engine2(lr::OP_SWIGLU_BWD2, dt, two, 1)) {
         const void* wt[1] = {W.tA_dn};
         RUN(nn_or_nt(lr::OP_NN_STORE, lr::OP_NT_STORE, dt, dmg, wt, 1, st, "dm = dd_r A_dn"));
         RUN(gemm(lr::OP_SWIGLU_BWD2, dt, two, 1, st, "SwiGLU recompute + backward"));

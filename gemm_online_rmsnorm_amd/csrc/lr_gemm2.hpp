@@ -1338,9 +1338,11 @@ __global__ __launch_bounds__(TL::NT, gemm2_min_waves<TL>()) void gemm2_kernel(Ge
   }
 #define LR_E(p, i, j) acc[SPLITN ? 0 : (p)][SPLITN ? (p) * FME + (i) : (i)][j]
   // The gate value g of element v of band i, fragment j, as it enters the
-  // SiLU: a bf16 value in every tile (the packed gate, or the accumulator
-  // rounded to bf16, as a bf16 GEMM would store it), so that the forward
-  // and the recompute in the backward agree bitwise whichever tiles they run.
+  // SiLU: a bf16 value in every tile of this engine (the packed gate, or the
+  // accumulator rounded alike, as a bf16 GEMM would store it), so that the
+  // forward and the recompute in the backward agree bitwise whichever of
+  // these tiles they run. (A shape's forward gate/up product runs on this
+  // engine exactly when its recompute does: the same K, N and extents.)
   auto gate_of = [&](int i, int j, int v) -> float {
     if constexpr (BDP) {
       const uint32_t w = gpk[i][j][v >> 1];
@@ -1365,21 +1367,6 @@ __global__ __launch_bounds__(TL::NT, gemm2_min_waves<TL>()) void gemm2_kernel(Ge
             LR_E(0, i, j)[v] = gg * sigmoid_f<bf16_t>(gg) * LR_E(1, i, j)[v];
         }
   }
-  if constexpr (EPI == EPI_SWIGLU_BWD) {
-#pragma unroll
-    for (int i = 0; i < FME; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float gg = LR_E(0, i, j)[v], uu = LR_E(1, i, j)[v], dm = LR_E(2, i, j)[v];
-          const float sg = sigmoid_f<bf16_t>(gg);
-          const float sl = gg * sg;
-          LR_E(0, i, j)[v] = sl * uu;
-          LR_E(1, i, j)[v] = dm * uu * sg * (1.0f + gg * (1.0f - sg));
-          LR_E(2, i, j)[v] = dm * sl;
-        }
-  }
 
   // Staging of one band's bf16 outputs for whole-row stores.
   static_assert(TL::WTN == 64 || TL::WTN == 32, "staging supports 32- and 64-column wave tiles");
@@ -1388,7 +1375,7 @@ __global__ __launch_bounds__(TL::NT, gemm2_min_waves<TL>()) void gemm2_kernel(Ge
   constexpr int PERL = 16 * CH / 64;  // chunks per lane per band
   auto swz_st = [](int row) { return RB == 128 ? epi_swz(row) : ((row >> 2) & 3); };
   unsigned char* sWb = lds + EL::ST + wave * epi_wave_bytes<TL>();
-  constexpr int NOUT = (EPI == EPI_SWIGLU_BWD || EPI == EPI_SWIGLU_BWD2) ? 3 : 1;
+  constexpr int NOUT = (EPI == EPI_SWIGLU_BWD2) ? 3 : 1;
   void* cq[NOUT];
   int64_t lq[NOUT];
   EpiOut<PERL> outs[NOUT];
@@ -1497,10 +1484,6 @@ __global__ __launch_bounds__(TL::NT, gemm2_min_waves<TL>()) void gemm2_kernel(Ge
             // dX = dY + gamma (dZ_n A) - coef H; gamma-gradient sums of acc H
             colacc[j][v] += x * hv[v];
             o[0][v] = rv[v] + gmv[j][v] * x - rs * hv[v];
-          } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-            o[0][v] = x;
-            o[1][v] = LR_E(1, i, j)[v];
-            o[2][v] = LR_E(2, i, j)[v];
           } else if constexpr (EPI == EPI_SWIGLU_BWD2) {
             // g, u recomputed in the accumulators, dm from HBM:
             // m = SiLU(g) u; dg = dm u sig(g)(1 + g(1 - sig(g))); du = dm SiLU(g)

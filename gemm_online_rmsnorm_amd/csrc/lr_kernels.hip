@@ -121,7 +121,6 @@ using P256x128 = Tile2<256, 128, 64, 2, 2, 2>;
 using P128x128 = Tile2<128, 128, 64, 2, 2, 2>;
 using P2x256x128 = Tile2<256, 128, 32, 4, 2, 3>;
 using P2x128x128 = Tile2<128, 128, 32, 2, 2, 3>;
-using P3x128x128 = Tile2<128, 128, 32, 2, 4, 3>;
 // Gate and up products side by side: 256 x (128 gate + 128 up) B rows,
 // 8 waves each running one pair on a 128 x 64 wave tile.
 using PS256x128 = Tile2<256, 256, 32, 2, 4, 3, 2>;
@@ -248,7 +247,6 @@ static bool eligible2(int op, const GemmDesc& d, int groups, int bk) {
     case OP_NN_RMSBWD: mc = 2u; break;
     case OP_NT_RMSBWD: break;
     case OP_TN_WGRAD: mc = 3u; break;
-    case OP_SWIGLU_BWD: mc = 32u; npair = 3; break;
     case OP_NT_SWIGLU:
     case OP_SWIGLU_BWD2: npair = 2; break;
     default: break;
@@ -361,7 +359,6 @@ static hipError_t run_gemm2(int op, const GemmDesc& d, int groups, hipStream_t s
         case 1: return launch2<PS256x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
         default: return launch2<P2x128x128, 2, 0u, EPI_SWIGLU>(d, 1, s);
       }
-    case OP_SWIGLU_BWD: return launch2<P3x128x128, 3, 32u, EPI_SWIGLU_BWD>(d, 1, s);
     case OP_SWIGLU_BWD2:
       switch (split_tile(d)) {
         case 4: return launch2<PBDP160x128, 2, 0u, EPI_SWIGLU_BWD2>(d, 1, s);
@@ -375,7 +372,7 @@ static hipError_t run_gemm2(int op, const GemmDesc& d, int groups, hipStream_t s
 }
 
 static int engine2_bk(int op) {
-  return (op == OP_NT_SWIGLU || op == OP_SWIGLU_BWD || op == OP_SWIGLU_BWD2) ? 32 : 64;
+  return (op == OP_NT_SWIGLU || op == OP_SWIGLU_BWD2) ? 32 : 64;
 }
 
 int gemm2_tile_m(int op, const GemmDesc& d, int groups) {
@@ -383,12 +380,14 @@ int gemm2_tile_m(int op, const GemmDesc& d, int groups) {
     const int t = split_tile(d);
     return t == 4 ? 160 : t == 0 ? 192 : ((t == 1 || t == 3) ? 256 : 128);
   }
-  if (op == OP_SWIGLU_BWD) return 128;
   return single_tile(d, groups) == 2 ? 128 : 256;
 }
 
+// The three-pair recompute (dm in the same tile) runs on the general engine
+// only: on this engine the recompute is a dm product and a two-pair tile,
+// which take the same shapes as the forward's gate/up tile.
 bool uses_engine2(int op, int dtype, const GemmDesc& d, int groups) {
-  return dtype == 1 && eligible2(op, d, groups, engine2_bk(op));
+  return dtype == 1 && op != OP_SWIGLU_BWD && eligible2(op, d, groups, engine2_bk(op));
 }
 
 int gemm_tile_m_used(int op, int dtype, const GemmDesc& d, int groups) {

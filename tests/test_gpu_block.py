@@ -24,12 +24,20 @@ CASES = {
                     fan_in_d=768, fan_in_F=1280, seed=23),
     "bf16-min": S("bf16-min", T=1, d=8, r=8, F=8, D=8, seed=24),
     "bf16-narrow": S("bf16-narrow", T=520, d=64, r=16, F=136, D=64, seed=25),
-    # gate/up grids of at least 256 tiles of 256 x 128 (the forward's tile
-    # in the 16384-token workloads) and 512 of 128 x 128 (the backward's,
-    # two per CU), ragged in rows and columns, with K = r of two k-tiles and
-    # of one
+    # gate/up grids of at least 256 block-diagonal tiles of 256 x 128, ragged
+    # in rows and columns, with K = r of two k-tiles and of one
     "bf16-gateup-r128": S("bf16-gateup-r128", T=4100, d=512, r=128, F=2112, D=512, seed=26),
     "bf16-gateup-r64": S("bf16-gateup-r64", T=4100, d=256, r=64, F=2104, D=256, seed=27),
+    # ... and of at least 512 packed tiles of 160 x 128 (two per CU, the
+    # tile of the 16384-token workloads), ragged in rows (100 of 160) and
+    # columns (40 of 128)
+    "bf16-gateup-packed-r128": S("bf16-gateup-packed-r128", T=4100, d=512, r=128, F=2600,
+                                 D=512, seed=33),
+    "bf16-gateup-packed-r64": S("bf16-gateup-packed-r64", T=4100, d=256, r=64, F=2600, D=256,
+                                seed=34),
+    # r a multiple of 32 but not of 64: gate/up tiles with k-tiles of 32,
+    # dm on the general engine before the two-pair recompute tile
+    "bf16-r96": S("bf16-r96", T=300, d=256, r=96, F=424, D=256, seed=32),
     # weight gradients of several shapes in one launch (dA_gu, dB_o, dA_o;
     # dA_qkv with dB_dn): with K split over per-problem partials (16 k-tiles)
     # and unsplit with ragged tiles (17 k-tiles, d and r not multiples of 256)

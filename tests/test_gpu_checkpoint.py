@@ -25,6 +25,9 @@ CASES = {
     "tiny-fp32": synth.config(1),
     "fp32-ragged": S("fp32-ragged", T=100, d=96, r=20, F=60, D=96, dtype="f32", seed=41),
     "bf16-ragged": S("bf16-ragged", T=300, d=320, r=80, F=424, D=320, seed=42),
+    # r a multiple of 32 but not of 64: the forward's gate/up tile and the
+    # backward's three-pair recompute tile (dm in the same tile) differ
+    "bf16-r96": S("bf16-r96", T=300, d=256, r=96, F=424, D=256, seed=45),
     # large tiles: the 256 x 256 residual tile and the gate/up tile of the
     # 16384-token workloads, with partial row and column tiles
     "bf16-large-tiles": S("bf16-large-tiles", T=1000, d=1024, r=256, F=2752, D=1024, P=2,
