@@ -38,6 +38,12 @@ CASES = {
     # r a multiple of 32 but not of 64: gate/up tiles with k-tiles of 32,
     # dm on the general engine before the two-pair recompute tile
     "bf16-r96": S("bf16-r96", T=300, d=256, r=96, F=424, D=256, seed=32),
+    # the split gate/up tiles (gate and up waves side by side) in both
+    # directions: 192 rows with k-tiles of 64 (grids of 256 such tiles but
+    # fewer of the larger ones), and 256 rows with k-tiles of 32 (r = 96)
+    "bf16-split192": S("bf16-split192", T=3000, d=256, r=64, F=2048, D=256, seed=35),
+    "bf16-split256-r96": S("bf16-split256-r96", T=4104, d=256, r=96, F=2056, D=256,
+                           seed=36),
     # weight gradients of several shapes in one launch (dA_gu, dB_o, dA_o;
     # dA_qkv with dB_dn): with K split over per-problem partials (16 k-tiles)
     # and unsplit with ragged tiles (17 k-tiles, d and r not multiples of 256)

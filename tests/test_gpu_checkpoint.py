@@ -34,6 +34,11 @@ CASES = {
                           seed=43),
     "bf16-share": S("bf16-share", T=200, d=192, r=192, F=320, D=768, partials=True,
                     fan_in_d=768, fan_in_F=1280, seed=44),
+    # the gate/up tiles of larger grids: packed 160 x 128 (the 16384-token
+    # workloads' tile), the 192-row split tile and the 256-row split tile
+    "bf16-packed": S("bf16-packed", T=4100, d=256, r=64, F=2600, D=256, seed=46),
+    "bf16-split192": S("bf16-split192", T=3000, d=256, r=64, F=2048, D=256, seed=47),
+    "bf16-split256-r96": S("bf16-split256-r96", T=4104, d=256, r=96, F=2056, D=256, seed=48),
 }
 
 
