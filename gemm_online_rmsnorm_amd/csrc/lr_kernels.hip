@@ -111,7 +111,8 @@ static hipError_t dispatch(int op, const GemmDesc& d, int groups, hipStream_t s)
 // k-tile. The large tile is 256 x 256 with 8 waves (two per SIMD, 128 x 64
 // each), so that one wave's barrier and LDS waits are covered by the other
 // wave's MFMAs; smaller grids fall back to 256 x 128 or 128 x 128 tiles with
-// 4 waves. The two- and three-pair GEMMs use k-tiles of 32 in three stages.
+// 4 waves. The gate/up pair GEMMs of small grids use k-tiles of 32 in
+// three stages.
 // ---------------------------------------------------------------------------
 using P256x256 = Tile2<256, 256, 64, 2, 4, 2>;
 // The same tile with separate rings: 3 stages of the A tile, 2 of the B
@@ -119,7 +120,6 @@ using P256x256 = Tile2<256, 256, 64, 2, 4, 2>;
 using P256x256a = Tile2<256, 256, 64, 2, 4, 2, 1, 3>;
 using P256x128 = Tile2<256, 128, 64, 2, 2, 2>;
 using P128x128 = Tile2<128, 128, 64, 2, 2, 2>;
-using P2x256x128 = Tile2<256, 128, 32, 4, 2, 3>;
 using P2x128x128 = Tile2<128, 128, 32, 2, 2, 3>;
 // Gate and up products side by side: 256 x (128 gate + 128 up) B rows,
 // 8 waves each running one pair on a 128 x 64 wave tile.
